@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the replicated FP8 cache-store + device-epoch fence on one MI355X.
+
+A step is one replay of the captured graph of the model shape: 61 sparse
+layers, each a kvpub_store of T=4096 tokens into R=2 replica caches of 8192
+64-slot pages followed by one kvpub_fence (so every part of the hot path runs:
+slot decode, row loads, tile amax, scale, e4m3 quantization, row packing, the
+R-way fan-out stores, the fence, graph replay).  Inputs are seeded N(0,1) bf16
+rows already resident in HBM; the cache layout is the one the library
+documents (656-byte Main-KV rows, 8448-byte Indexer-K pages).
+
+Printed: one JSON line with tokens/s (value), the store kernel's achieved HBM
+bandwidth against the 8 TB/s peak (roofline), the fence cost per layer, and
+the CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+READ_BYTES_PER_TOKEN = (512 + 64 + 128) * 2         # bf16 rows read
+WRITE_BYTES_PER_TOKEN_PER_REPLICA = 656 + 128 + 4   # Main-KV row + Indexer-K codes + scale
+
+
+def alg_bytes(valid_tokens, replicas):
+    return valid_tokens * (READ_BYTES_PER_TOKEN + replicas * WRITE_BYTES_PER_TOKEN_PER_REPLICA)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prefill / heavy-tail store-only figures")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle baseline sample")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on a given torch stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.stream)
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the replicas of this path are buffers in one GPU's "
+              "HBM and no multi-GPU run is part of this build; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from replicated_fp8_sparse_amd import kvpub, workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = kvpub.load()
+    dev_name = torch.cuda.get_device_name(0)
+
+    L, T = W.GRAPH_LAYERS, W.GRAPH_T
+    layout = W.graph_layout()
+    R = layout.replicas
+    print(f"[bench] {dev_name}: graph workload {L} layers x T={T}, R={R}, pages={layout.num_pages}",
+          file=sys.stderr, flush=True)
+
+    main_bufs = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    idx_bufs = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    for b in main_bufs:
+        layout.fill_device(b, "main")
+    for b in idx_bufs:
+        layout.fill_device(b, "idx")
+    cfg = kvpub.kvpub_config_init(R, L, layout.num_pages)
+    st, ctx = kvpub.kvpub_create(cfg, [b.data_ptr() for b in main_bufs], [b.data_ptr() for b in idx_bufs])
+    kvpub.check(st, "kvpub_create")
+
+    lat = torch.empty((L, T, 512), dtype=torch.bfloat16, device="cuda")
+    rope = torch.empty((L, T, 64), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((L, T, 128), dtype=torch.bfloat16, device="cuda")
+    W.graph_fill_inputs_device(lat, rope, idx, seed=5, replay=0)
+    slots_np = W.graph_slots()
+    slots = torch.from_numpy(slots_np).to("cuda")
+    valid = int(((slots_np >= 0) & (slots_np < layout.capacity)).sum())
+
+    ios = [kvpub.layer_io(lat[l].data_ptr(), rope[l].data_ptr(), idx[l].data_ptr(),
+                          slots.data_ptr(), T, l) for l in range(L)]
+    st, graph = kvpub.kvpub_graph_create(ctx, ios, 0)
+    kvpub.check(st, "kvpub_graph_create")
+
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+
+    # --- the timed steps: K replays of the full store + fence graph -------------
+    for _ in range(args.warmup):
+        kvpub.check(kvpub.kvpub_graph_replay(graph, sh))
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    with Timer(torch, stream) as tm:
+        for _ in range(args.steps):
+            kvpub.kvpub_graph_replay(graph, sh)
+    step_ms = tm.ms / args.steps
+    st, epoch = kvpub.kvpub_epoch_read(ctx, 0)
+    kvpub.check(st)
+    assert epoch == L * (args.warmup + args.steps), epoch
+    tokens_per_s = valid * L / (step_ms * 1e-3)
+
+    # --- store kernel alone: the same 61 stores captured without fences ---------
+    g_store = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g_store, stream=stream):
+            for l in range(L):
+                kvpub.check(kvpub.kvpub_store(ctx, l, T, lat[l].data_ptr(), 512, rope[l].data_ptr(), 64,
+                                              idx[l].data_ptr(), 128, slots.data_ptr(), sh))
+    reps = max(4, args.steps // 4)
+    for _ in range(2):
+        g_store.replay()
+    with Timer(torch, stream) as ts:
+        for _ in range(reps):
+            g_store.replay()
+    store_us = ts.ms * 1e3 / (reps * L)
+    store_bytes = alg_bytes(valid, R)
+    store_gbps = store_bytes / (store_us * 1e-6) / 1e9
+
+    # --- fence alone: 61 fences captured back to back --------------------------
+    g_fence = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g_fence, stream=stream):
+            for l in range(L):
+                kvpub.check(kvpub.kvpub_fence(ctx, 0, sh))
+    for _ in range(2):
+        g_fence.replay()
+    with Timer(torch, stream) as tf:
+        for _ in range(reps):
+            g_fence.replay()
+    fence_us_alone = tf.ms * 1e3 / (reps * L)
+    fence_us_in_step = (step_ms * 1e3 - store_us * L) / L
+    st, invalid, flags = kvpub.kvpub_error_read(ctx, False)
+    kvpub.check(st)
+    assert invalid == 0 and flags == 0
+
+    extras = {}
+    if not args.no_extras:
+        extras = store_only_extras(torch, kvpub, W, stream)
+
+    result = {
+        "metric": "cache-store tokens/sec and achieved HBM GB/s (% of peak); fence µs/layer",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "graph replay, model shape: 61 sparse layers x T=4096 tokens, R=2 replicas, "
+                        "8192 pages x 64 slots per replica per layer-cache, store + fence per layer",
+            "layers": L, "tokens_per_layer": T, "valid_tokens_per_layer": valid, "replicas": R,
+            "pages": layout.num_pages, "inputs": "bf16 N(0,1), latent 512 + rope 64 + indexer 128",
+            "cache": "e4m3fn codes + fp32 tile scales; 656 B Main-KV row, 8448 B Indexer-K page",
+            "device": dev_name,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "store_kernel<2>",
+            "achieved": round(store_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(store_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "alg_bytes_per_launch": store_bytes,
+            "avg_launch_us": round(store_us, 3),
+            "how": "HIP events around replays of a graph of the 61 store launches alone",
+        },
+        "fence_us_per_layer": {
+            "in_step": round(fence_us_in_step, 3),
+            "alone": round(fence_us_alone, 3),
+            "how": "in_step = (step time - 61 x store time) / 61; alone = graph of 61 fences / 61",
+        },
+        "store_us_per_layer": round(store_us, 3),
+    }
+    if extras:
+        result["store_only"] = extras
+
+    kvpub.kvpub_graph_destroy(graph)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(lat, rope, idx, slots_np, layout, args.cpu_seconds)
+
+    kvpub.check(kvpub.kvpub_destroy(ctx))
+    print(json.dumps(result), flush=True)
+
+
+def store_only_extras(torch, kvpub, W, stream):
+    """Store-kernel bandwidth on the prefill (T=8192, R=4) and heavy-tail (T=32768, R=4)
+    workloads: eager back-to-back launches over rotated input copies, HIP events."""
+    out = {}
+    sh = stream.cuda_stream
+    for name, fn, copies in (("prefill_T8192_R4", W.prefill, 8), ("heavy_T32768_R4", W.heavy, 8)):
+        layout, x = fn()
+        print(f"[bench] store-only {name}", file=sys.stderr, flush=True)
+        R = layout.replicas
+        mb = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        ib = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        for b in mb:
+            layout.fill_device(b, "main")
+        for b in ib:
+            layout.fill_device(b, "idx")
+        cfg = kvpub.kvpub_config_init(R, 1, layout.num_pages)
+        st, ctx = kvpub.kvpub_create(cfg, [b.data_ptr() for b in mb], [b.data_ptr() for b in ib])
+        kvpub.check(st)
+        T = x.slots.size
+        lat = torch.from_numpy(x.latent.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+        rope = torch.from_numpy(x.rope.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+        idx = torch.from_numpy(x.indexer.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+        slots = torch.from_numpy(x.slots).to("cuda")
+        valid = int(((x.slots >= 0) & (x.slots < layout.capacity)).sum())
+
+        def launch(c):
+            return kvpub.kvpub_store(ctx, 0, T, lat[c].data_ptr(), 512, rope[c].data_ptr(), 64,
+                                     idx[c].data_ptr(), 128, slots.data_ptr(), sh)
+
+        for c in range(copies):
+            kvpub.check(launch(c))
+        n = 8 * copies
+        with Timer(torch, stream) as tm:
+            for i in range(n):
+                launch(i % copies)
+        us = tm.ms * 1e3 / n
+        b = alg_bytes(valid, R)
+        out[name] = {"avg_launch_us": round(us, 3), "alg_bytes": b,
+                     "gbps": round(b / (us * 1e-6) / 1e9, 1),
+                     "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "tokens_per_s": round(valid / (us * 1e-6), 1)}
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+        del mb, ib, lat, rope, idx
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(lat, rope, idx, slots_np, layout, seconds):
+    """The CPU oracle (single-threaded C, as it stands) on a bounded sample of the
+    same workload: the graph workload's layers one after another, into host
+    replicas of one layer-cache, until about `seconds` of CPU time."""
+    import oracle
+    orc = oracle.get()
+    L = lat.shape[0]
+    m0, i0 = oracle_host_layer(layout)
+    mains = [m0.copy() for _ in range(layout.replicas)]
+    idxs = [i0.copy() for _ in range(layout.replicas)]
+    done_tokens = 0
+    elapsed = 0.0
+    layers = 0
+    for l in range(L):
+        x_l = lat[l].cpu().view(torch_int16()).numpy().view(np.uint16)
+        x_r = rope[l].cpu().view(torch_int16()).numpy().view(np.uint16)
+        x_i = idx[l].cpu().view(torch_int16()).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        orc.store(mains, idxs, num_pages=layout.num_pages,
+                  main_page_stride=layout.main_page_stride, main_layer_stride=layout.main_layer_stride,
+                  idx_page_stride=layout.idx_page_stride, idx_layer_stride=layout.idx_layer_stride,
+                  layer=0, latent=x_l, rope=x_r, indexer=x_i, slot_mapping=slots_np)
+        elapsed += time.perf_counter() - t0
+        done_tokens += int(((slots_np >= 0) & (slots_np < layout.capacity)).sum())
+        layers += 1
+        if elapsed >= seconds:
+            break
+    return {"value": round(done_tokens / elapsed, 1), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{layers} layers of the graph workload (T=4096, R=2, 8192 pages), "
+                      f"single-threaded C oracle, {elapsed:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+def torch_int16():
+    import torch
+    return torch.int16
+
+
+def oracle_host_layer(layout):
+    from replicated_fp8_sparse_amd.workloads import CacheLayout
+    one = CacheLayout(replicas=layout.replicas, layers=1, num_pages=layout.num_pages)
+    return one.fill_host()
+
+
+if __name__ == "__main__":
+    main()

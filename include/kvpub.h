@@ -1,0 +1,227 @@
+/*
+ * kvpub.h -- replicated FP8 KV cache-store and device-epoch fence (MI355X, gfx950).
+ *
+ * C ABI of libkvpub.so.  Plain pointers and sizes only: device pointers are
+ * HIP device addresses (for example torch tensors' data_ptr()), streams are
+ * hipStream_t values passed as void*.
+ *
+ * What the library does, and where the pages define it:
+ *   - kvpub_store: quantize each new token's final Main-KV row (bf16 latent
+ *     [512] + bf16 RoPE [64]) and Indexer-K row (bf16 [128]) to FP8 once and
+ *     write the bytes straight into every replica of a paged KV cache, with
+ *     no gather and no receive-side insert (vLLM PR #52863 "[Kernel][PCP]
+ *     Publish replicated KV updates through PyTorch symmetric memory",
+ *     Summary, the "THIS PR: publish final rows directly" diagram, and the
+ *     Design bullet on fused cache-store kernels writing to every peer).
+ *     The replicas must end byte-identical to what gather-then-insert would
+ *     give, padded and invalid slots and guard bytes included (same page,
+ *     "Correctness and current-head validation").
+ *   - kvpub_fence: one launch that advances a device-resident epoch with a
+ *     system-scope release and then acquire-waits for every participant, so
+ *     that a captured graph advances the epoch on every replay (vLLM PR
+ *     #54030 "[Perf][PCP] Fuse direct-KV publication fence", its commit list
+ *     and Motivation; PR #52863 Design bullet on the device-epoch barrier and
+ *     separate DBO lanes).
+ *   - kvpub_graph_create / kvpub_graph_replay: the store + fence sequence of
+ *     several layers captured once in a hipGraph and replayed (PR #54030
+ *     commit list: a two-GPU replay test checks that every replay advances the
+ *     epoch; PR #52863 Design: graph replay is supported).
+ *   - all-or-nothing creation and fail-closed fences (PR #54030 commit list:
+ *     opt-in allocation is all-or-nothing at startup; a fence timeout must not
+ *     let work continue).
+ *
+ * Byte layout (the pages name the FP8 Main-KV format, fp8_ds_mla, without
+ * printing its bytes; this is the library's reading):
+ *   Main-KV row, 656 B, at replica + layer*main_layer_stride
+ *                          + page*main_page_stride + offset*656:
+ *     [0,512)   e4m3fn codes of latent[0..511]
+ *     [512,528) fp32 scales of latent tiles [0,128) [128,256) [256,384) [384,512)
+ *     [528,656) RoPE bf16 bit patterns, copied unchanged
+ *   Indexer-K, at replica + layer*idx_layer_stride + page*idx_page_stride:
+ *     [offset*128, +128)     e4m3fn codes of indexer[0..127]
+ *     [8192 + offset*4, +4)  fp32 scale of the indexer row
+ *   Scaling: per 128-element tile, scale = amax / 448 (binary32), code =
+ *   e4m3fn(x / scale) with x / scale rounded to binary32, then rounded to
+ *   nearest-even e4m3fn saturating at +-448; an all-zero tile stores scale
+ *   +0 and codes 0x00.  All multi-byte fields are little-endian.
+ *   Slots: slot s lives in page s / 64 at offset s % 64.  s == -1 marks a
+ *   padded token: it is neither read nor written.  Any other slot outside
+ *   [0, num_pages*64) is skipped and counted (kvpub_error_read).
+ *
+ * Errors: functions never abort and no C++ exception crosses this ABI.
+ * Argument problems are reported before anything is launched, so nothing is
+ * written.  Device-side problems (invalid slots, a fence that timed out) are
+ * recorded in the context's device words and reported by kvpub_error_read.
+ */
+#ifndef KVPUB_H
+#define KVPUB_H
+
+#include <stdint.h>
+
+#if defined(KVPUB_BUILD_SHARED)
+#define KVPUB_API __attribute__((visibility("default")))
+#else
+#define KVPUB_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVPUB_ABI_VERSION 1u
+
+#define KVPUB_SLOTS_PER_PAGE 64u
+#define KVPUB_LATENT_DIM 512u
+#define KVPUB_ROPE_DIM 64u
+#define KVPUB_INDEXER_DIM 128u
+#define KVPUB_MAIN_ROW_BYTES 656u
+#define KVPUB_MAIN_PAGE_BYTES (64u * 656u)            /* 41984 */
+#define KVPUB_IDX_PAGE_BYTES (64u * 128u + 64u * 4u)  /* 8448 */
+#define KVPUB_IDX_SCALES_OFFSET (64u * 128u)          /* 8192 */
+#define KVPUB_MAX_REPLICAS 8u
+#define KVPUB_MAX_LANES 64u
+#define KVPUB_MAX_PARTICIPANTS 8u
+#define KVPUB_MAX_TOKENS (1ll << 30)
+
+typedef struct kvpub_ctx kvpub_ctx;
+typedef struct kvpub_graph kvpub_graph;
+typedef void *kvpub_stream_t; /* hipStream_t; NULL = the null stream */
+
+typedef enum {
+    KVPUB_OK = 0,
+    KVPUB_ERR_INVALID_ARG = 1,   /* bad argument; nothing was launched */
+    KVPUB_ERR_OUT_OF_MEMORY = 2, /* an allocation failed; nothing is left allocated */
+    KVPUB_ERR_UNSUPPORTED = 3,   /* device is not gfx950 */
+    KVPUB_ERR_HIP = 4,           /* a HIP runtime call failed */
+    KVPUB_ERR_CAPTURING = 5,     /* a synchronizing call while a stream capture is active */
+    KVPUB_ERR_FENCE_TIMEOUT = 6  /* a fence timed out: the context is poisoned */
+} kvpub_status;
+
+/* Sticky device flags reported by kvpub_error_read. */
+#define KVPUB_FLAG_FENCE_TIMEOUT 0x1u /* a fence gave up waiting */
+#define KVPUB_FLAG_POISONED 0x2u      /* later stores and fences do nothing */
+
+typedef struct {
+    uint32_t struct_size;       /* sizeof(kvpub_config) */
+    uint32_t num_replicas;      /* R, 1..8 */
+    uint32_t num_layers;        /* L >= 1 */
+    uint32_t block_size;        /* slots per page; must be 64 */
+    uint64_t num_pages;         /* pages per replica per layer, >= 1 */
+    uint64_t main_page_stride;  /* bytes, >= 41984, multiple of 16 */
+    uint64_t main_layer_stride; /* bytes, >= num_pages*main_page_stride, multiple of 16 (ignored if L == 1) */
+    uint64_t idx_page_stride;   /* bytes, >= 8448, multiple of 16 */
+    uint64_t idx_layer_stride;  /* bytes, >= num_pages*idx_page_stride, multiple of 16 (ignored if L == 1) */
+    uint32_t num_lanes;         /* fence lanes (one per overlapped micro-batch), 1..64 */
+    uint32_t num_participants;  /* fence participants, 1..8; > 1 only with host-driven peers (tests) */
+    uint64_t fence_timeout_ns;  /* 0 = 5 s */
+    int32_t device;             /* HIP device ordinal */
+    uint32_t flags;             /* reserved, must be 0 */
+} kvpub_config;
+
+/* Fill *cfg with defaults for R replicas of L layers of num_pages dense pages:
+ * page strides 41984 / 8448, layer strides num_pages * page stride, one lane,
+ * one participant, device 0. */
+KVPUB_API void kvpub_config_init(kvpub_config *cfg, uint32_t num_replicas, uint32_t num_layers,
+                       uint64_t num_pages);
+
+/* Create a context over R caller-owned replica buffers.
+ * main_bases[r] / idx_bases[r]: device pointers, 16-byte aligned, each at least
+ * (L-1)*layer_stride + num_pages*page_stride bytes.  The caller keeps ownership
+ * and must keep them alive until kvpub_destroy.  The context owns only its
+ * device words (epochs, participant signals, error counters) on `device`.
+ * All-or-nothing: on any failure every resource it made is released and *out
+ * is set to NULL.  Returns KVPUB_ERR_UNSUPPORTED unless the device is gfx950. */
+KVPUB_API kvpub_status kvpub_create(const kvpub_config *cfg, void *const *main_bases,
+                          void *const *idx_bases, kvpub_ctx **out);
+
+/* Quantize num_tokens tokens' final rows and write them into every replica's
+ * layer `layer`, asynchronously on `stream`.
+ *   latent:  bf16 [T, 512], row stride latent_row_stride elements
+ *   rope:    bf16 [T, 64],  row stride rope_row_stride elements
+ *   indexer: bf16 [T, 128], row stride indexer_row_stride elements
+ *   slot_mapping: int64 [T] device array (-1 = padded token)
+ * Inputs are device pointers, 16-byte aligned, with row strides that are
+ * multiples of 8 elements and at least the row width; slot_mapping is 8-byte
+ * aligned.  Valid slots within one call must be distinct and inputs finite.
+ * num_tokens == 0 returns KVPUB_OK and launches nothing.  No allocation and no
+ * synchronization: safe under stream capture.  Inputs must stay alive until
+ * the stream work completes. */
+KVPUB_API kvpub_status kvpub_store(kvpub_ctx *ctx, uint32_t layer, int64_t num_tokens,
+                         const void *latent, int64_t latent_row_stride,
+                         const void *rope, int64_t rope_row_stride,
+                         const void *indexer, int64_t indexer_row_stride,
+                         const int64_t *slot_mapping, kvpub_stream_t stream);
+
+/* One fence on `lane`, asynchronously on `stream`: a single one-wavefront
+ * kernel that adds 1 to the lane's device epoch with a system-scope release,
+ * publishes the new value as this participant's signal, and acquire-waits
+ * until every participant's signal has reached it.  The expected value is
+ * never a kernel argument, so a captured fence advances the epoch on every
+ * replay.  If the wait exceeds fence_timeout_ns the kernel records
+ * KVPUB_FLAG_FENCE_TIMEOUT | KVPUB_FLAG_POISONED and returns; from then on
+ * stores and fences of this context write nothing (fail-closed).  No
+ * allocation and no synchronization: safe under stream capture. */
+KVPUB_API kvpub_status kvpub_fence(kvpub_ctx *ctx, uint32_t lane, kvpub_stream_t stream);
+
+/* One layer of a captured sequence. */
+typedef struct {
+    const void *latent;
+    const void *rope;
+    const void *indexer;
+    int64_t latent_row_stride;
+    int64_t rope_row_stride;
+    int64_t indexer_row_stride;
+    const int64_t *slot_mapping;
+    int64_t num_tokens;
+    uint32_t layer;
+    uint32_t reserved; /* must be 0 */
+} kvpub_layer_io;
+
+/* Capture n x (kvpub_store(io[i]), kvpub_fence(lane)) once into a hipGraph
+ * (on a private stream) and instantiate it.  The graph binds the pointers in
+ * io: to publish new data, rewrite those buffers before a replay.  They must
+ * outlive the graph.  Argument checks as for kvpub_store, done for every layer
+ * before capture begins. */
+KVPUB_API kvpub_status kvpub_graph_create(kvpub_ctx *ctx, const kvpub_layer_io *io, uint32_t n,
+                                uint32_t lane, kvpub_graph **out);
+
+/* Launch the instantiated graph once on `stream` (asynchronous). */
+KVPUB_API kvpub_status kvpub_graph_replay(kvpub_graph *graph, kvpub_stream_t stream);
+
+/* Release a graph (waits for nothing; do not destroy while a replay may run). */
+KVPUB_API kvpub_status kvpub_graph_destroy(kvpub_graph *graph);
+
+/* Synchronize the device, then read the lane's epoch (number of fences that
+ * ran on it).  KVPUB_ERR_CAPTURING if a capture is active on the calling thread. */
+KVPUB_API kvpub_status kvpub_epoch_read(kvpub_ctx *ctx, uint32_t lane, uint64_t *out);
+
+/* Synchronize the device, then read the invalid-slot count and the sticky
+ * flags (either output may be NULL).  clear != 0 resets the invalid-slot
+ * count; the flags stay set for the context's lifetime.  Returns
+ * KVPUB_ERR_FENCE_TIMEOUT if KVPUB_FLAG_FENCE_TIMEOUT is set, else KVPUB_OK. */
+KVPUB_API kvpub_status kvpub_error_read(kvpub_ctx *ctx, uint64_t *invalid_slots, uint32_t *flags,
+                              int clear);
+
+/* Host address of participant p's signal word on `lane` (1 <= p <
+ * num_participants).  It lives in host-coherent memory that the fence kernel
+ * reads with system-scope acquire loads; a host thread stands in for peer p by
+ * storing the epoch values it publishes.  Only meaningful with
+ * num_participants > 1 (one GPU has no real peers). */
+KVPUB_API kvpub_status kvpub_participant_signal(kvpub_ctx *ctx, uint32_t lane, uint32_t p,
+                                      volatile uint64_t **out);
+
+/* Synchronize the device and release the context's resources.  NULL is OK.
+ * The replica buffers are the caller's and are left untouched. */
+KVPUB_API kvpub_status kvpub_destroy(kvpub_ctx *ctx);
+
+/* Static description of a status code. */
+KVPUB_API const char *kvpub_strerror(kvpub_status status);
+
+/* KVPUB_ABI_VERSION of the loaded library. */
+KVPUB_API uint32_t kvpub_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPUB_H */

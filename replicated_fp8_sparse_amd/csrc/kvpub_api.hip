@@ -1,0 +1,425 @@
+// C-ABI host side of libkvpub: argument checks, context lifetime, launches,
+// graph capture.  Nothing here allocates or synchronizes on the store / fence
+// path; creation is all-or-nothing (vLLM PR #54030 "[Perf][PCP] Fuse
+// direct-KV publication fence", commit list: opt-in allocation either fully
+// succeeds at startup or leaves nothing behind; teardown drops every view).
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "kvpub.h"
+#include "kvpub_internal.h"
+
+using kvpub::FenceParams;
+using kvpub::StoreParams;
+
+struct kvpub_ctx {
+    kvpub_config cfg;
+    uint8_t* main_base[KVPUB_MAX_REPLICAS];
+    uint8_t* idx_base[KVPUB_MAX_REPLICAS];
+    uint8_t* words;            // device: status, invalid count, epochs, (P == 1) signals
+    uint64_t* host_signals;    // P > 1: host-coherent signals [lanes][P] (kSignalStride apart)
+    uint64_t* host_signals_dev;
+    uint64_t timeout_ticks;
+    hipStream_t capture_stream;
+};
+
+struct kvpub_graph {
+    kvpub_ctx* ctx;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+namespace {
+
+constexpr uint64_t kDefaultTimeoutNs = 5000000000ull;
+
+size_t words_bytes(const kvpub_config& c) {
+    size_t b = kvpub::kEpochOffset + (size_t)c.num_lanes * kvpub::kLine;
+    if (c.num_participants == 1) b += (size_t)c.num_lanes * kvpub::kLine;
+    return b;
+}
+
+uint64_t* epoch_ptr(kvpub_ctx* c, uint32_t lane) {
+    return reinterpret_cast<uint64_t*>(c->words + kvpub::kEpochOffset + (size_t)lane * kvpub::kLine);
+}
+
+uint64_t* signals_dev_ptr(kvpub_ctx* c, uint32_t lane) {
+    const uint32_t P = c->cfg.num_participants;
+    if (P == 1)
+        return reinterpret_cast<uint64_t*>(c->words + kvpub::kEpochOffset +
+                                           (size_t)(c->cfg.num_lanes + lane) * kvpub::kLine);
+    return c->host_signals_dev + (size_t)lane * P * kvpub::kSignalStride;
+}
+
+// Sets the context's device current for the lifetime of the guard.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) { ok = false; prev = -1; return; }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+// Test hook: KVPUB_TEST_FAIL_ALLOC_AT=k makes the k-th allocation of a
+// kvpub_create call fail (k >= 1), to exercise the all-or-nothing cleanup.
+struct AllocCounter {
+    int fail_at = 0;
+    int n = 0;
+    AllocCounter() {
+        const char* s = std::getenv("KVPUB_TEST_FAIL_ALLOC_AT");
+        fail_at = s ? std::atoi(s) : 0;
+    }
+    bool next_fails() { return ++n == fail_at; }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kvpub_status map_hip(hipError_t e) {
+    switch (e) {
+        case hipSuccess: return KVPUB_OK;
+        case hipErrorOutOfMemory: return KVPUB_ERR_OUT_OF_MEMORY;
+        case hipErrorStreamCaptureUnsupported:
+        case hipErrorStreamCaptureInvalidated:
+        case hipErrorStreamCaptureImplicit:
+        case hipErrorCapturedEvent:
+        case hipErrorStreamCaptureWrongThread:
+            return KVPUB_ERR_CAPTURING;
+        default: return KVPUB_ERR_HIP;
+    }
+}
+
+kvpub_status check_config(const kvpub_config* c) {
+    if (!c || c->struct_size != sizeof(kvpub_config)) return KVPUB_ERR_INVALID_ARG;
+    if (c->num_replicas < 1 || c->num_replicas > KVPUB_MAX_REPLICAS) return KVPUB_ERR_INVALID_ARG;
+    if (c->num_layers < 1 || c->block_size != KVPUB_SLOTS_PER_PAGE) return KVPUB_ERR_INVALID_ARG;
+    if (c->num_pages < 1 || c->num_pages > (1ull << 40)) return KVPUB_ERR_INVALID_ARG;
+    if (c->main_page_stride < KVPUB_MAIN_PAGE_BYTES || c->main_page_stride % 16) return KVPUB_ERR_INVALID_ARG;
+    if (c->idx_page_stride < KVPUB_IDX_PAGE_BYTES || c->idx_page_stride % 16) return KVPUB_ERR_INVALID_ARG;
+    if (c->num_layers > 1) {
+        if (c->main_layer_stride % 16 || c->idx_layer_stride % 16) return KVPUB_ERR_INVALID_ARG;
+        if (c->main_layer_stride / c->main_page_stride < c->num_pages) return KVPUB_ERR_INVALID_ARG;
+        if (c->idx_layer_stride / c->idx_page_stride < c->num_pages) return KVPUB_ERR_INVALID_ARG;
+    }
+    if (c->num_lanes < 1 || c->num_lanes > KVPUB_MAX_LANES) return KVPUB_ERR_INVALID_ARG;
+    if (c->num_participants < 1 || c->num_participants > KVPUB_MAX_PARTICIPANTS) return KVPUB_ERR_INVALID_ARG;
+    if (c->device < 0 || c->flags != 0) return KVPUB_ERR_INVALID_ARG;
+    return KVPUB_OK;
+}
+
+kvpub_status check_store(const kvpub_ctx* ctx, uint32_t layer, int64_t T, const void* latent,
+                         int64_t ls, const void* rope, int64_t rs, const void* indexer,
+                         int64_t is, const int64_t* slots) {
+    if (!ctx) return KVPUB_ERR_INVALID_ARG;
+    if (layer >= ctx->cfg.num_layers) return KVPUB_ERR_INVALID_ARG;
+    if (T < 0 || T > KVPUB_MAX_TOKENS) return KVPUB_ERR_INVALID_ARG;
+    if (T == 0) return KVPUB_OK;
+    if (!latent || !rope || !indexer || !slots) return KVPUB_ERR_INVALID_ARG;
+    if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(indexer, 16) || !aligned(slots, 8))
+        return KVPUB_ERR_INVALID_ARG;
+    if (ls < (int64_t)KVPUB_LATENT_DIM || ls % 8) return KVPUB_ERR_INVALID_ARG;
+    if (rs < (int64_t)KVPUB_ROPE_DIM || rs % 8) return KVPUB_ERR_INVALID_ARG;
+    if (is < (int64_t)KVPUB_INDEXER_DIM || is % 8) return KVPUB_ERR_INVALID_ARG;
+    return KVPUB_OK;
+}
+
+StoreParams store_params(kvpub_ctx* ctx, uint32_t layer, int64_t T, const void* latent, int64_t ls,
+                         const void* rope, int64_t rs, const void* indexer, int64_t is,
+                         const int64_t* slots) {
+    StoreParams p;
+    std::memset(&p, 0, sizeof p);
+    p.latent = static_cast<const uint16_t*>(latent);
+    p.rope = static_cast<const uint16_t*>(rope);
+    p.indexer = static_cast<const uint16_t*>(indexer);
+    p.latent_stride = ls;
+    p.rope_stride = rs;
+    p.indexer_stride = is;
+    p.slots = slots;
+    p.num_tokens = T;
+    p.capacity = (int64_t)(ctx->cfg.num_pages * KVPUB_SLOTS_PER_PAGE);
+    p.main_page_stride = ctx->cfg.main_page_stride;
+    p.idx_page_stride = ctx->cfg.idx_page_stride;
+    for (uint32_t r = 0; r < ctx->cfg.num_replicas; ++r) {
+        p.main_base[r] = ctx->main_base[r] + (uint64_t)layer * ctx->cfg.main_layer_stride;
+        p.idx_base[r] = ctx->idx_base[r] + (uint64_t)layer * ctx->cfg.idx_layer_stride;
+    }
+    p.invalid_count = reinterpret_cast<unsigned long long*>(ctx->words + kvpub::kInvalidOffset);
+    p.status = reinterpret_cast<const uint32_t*>(ctx->words + kvpub::kStatusOffset);
+    return p;
+}
+
+FenceParams fence_params(kvpub_ctx* ctx, uint32_t lane) {
+    FenceParams f;
+    f.epoch = epoch_ptr(ctx, lane);
+    f.signals = signals_dev_ptr(ctx, lane);
+    f.num_participants = ctx->cfg.num_participants;
+    f.self = 0;
+    f.status = reinterpret_cast<uint32_t*>(ctx->words + kvpub::kStatusOffset);
+    f.timeout_ticks = ctx->timeout_ticks;
+    return f;
+}
+
+void release(kvpub_ctx* c) {
+    if (!c) return;
+    if (c->capture_stream) (void)hipStreamDestroy(c->capture_stream);
+    if (c->host_signals) (void)hipHostFree(c->host_signals);
+    if (c->words) (void)hipFree(c->words);
+    delete c;
+}
+
+kvpub_status sync_device() {
+    return map_hip(hipDeviceSynchronize());
+}
+
+}  // namespace
+
+extern "C" {
+
+KVPUB_API void kvpub_config_init(kvpub_config* cfg, uint32_t num_replicas, uint32_t num_layers,
+                                 uint64_t num_pages) {
+    if (!cfg) return;
+    std::memset(cfg, 0, sizeof *cfg);
+    cfg->struct_size = sizeof(kvpub_config);
+    cfg->num_replicas = num_replicas;
+    cfg->num_layers = num_layers;
+    cfg->block_size = KVPUB_SLOTS_PER_PAGE;
+    cfg->num_pages = num_pages;
+    cfg->main_page_stride = KVPUB_MAIN_PAGE_BYTES;
+    cfg->main_layer_stride = num_pages * KVPUB_MAIN_PAGE_BYTES;
+    cfg->idx_page_stride = KVPUB_IDX_PAGE_BYTES;
+    cfg->idx_layer_stride = num_pages * KVPUB_IDX_PAGE_BYTES;
+    cfg->num_lanes = 1;
+    cfg->num_participants = 1;
+    cfg->fence_timeout_ns = 0;
+    cfg->device = 0;
+    cfg->flags = 0;
+}
+
+KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_bases,
+                                   void* const* idx_bases, kvpub_ctx** out) {
+    if (!out) return KVPUB_ERR_INVALID_ARG;
+    *out = nullptr;
+    kvpub_status st = check_config(cfg);
+    if (st != KVPUB_OK) return st;
+    if (!main_bases || !idx_bases) return KVPUB_ERR_INVALID_ARG;
+    for (uint32_t r = 0; r < cfg->num_replicas; ++r) {
+        if (!main_bases[r] || !idx_bases[r]) return KVPUB_ERR_INVALID_ARG;
+        if (!aligned(main_bases[r], 16) || !aligned(idx_bases[r], 16)) return KVPUB_ERR_INVALID_ARG;
+    }
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return KVPUB_ERR_HIP;
+    if (cfg->device >= ndev) return KVPUB_ERR_INVALID_ARG;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, cfg->device) != hipSuccess) return KVPUB_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KVPUB_ERR_UNSUPPORTED;
+
+    DeviceGuard guard(cfg->device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+
+    kvpub_ctx* c = new (std::nothrow) kvpub_ctx;
+    if (!c) return KVPUB_ERR_OUT_OF_MEMORY;
+    std::memset(c, 0, sizeof *c);
+    c->cfg = *cfg;
+    for (uint32_t r = 0; r < cfg->num_replicas; ++r) {
+        c->main_base[r] = static_cast<uint8_t*>(main_bases[r]);
+        c->idx_base[r] = static_cast<uint8_t*>(idx_bases[r]);
+    }
+
+    AllocCounter alloc;
+    const size_t wb = words_bytes(*cfg);
+    hipError_t e = alloc.next_fails() ? hipErrorOutOfMemory : hipMalloc(&c->words, wb);
+    if (e != hipSuccess) { c->words = nullptr; release(c); return map_hip(e); }
+    e = hipMemset(c->words, 0, wb);
+    if (e != hipSuccess) { release(c); return map_hip(e); }
+
+    if (cfg->num_participants > 1) {
+        const size_t hb = (size_t)cfg->num_lanes * cfg->num_participants * kvpub::kLine;
+        e = alloc.next_fails() ? hipErrorOutOfMemory
+                               : hipHostMalloc(reinterpret_cast<void**>(&c->host_signals), hb,
+                                               hipHostMallocCoherent | hipHostMallocMapped);
+        if (e != hipSuccess) { c->host_signals = nullptr; release(c); return map_hip(e); }
+        std::memset(c->host_signals, 0, hb);
+        e = hipHostGetDevicePointer(reinterpret_cast<void**>(&c->host_signals_dev), c->host_signals, 0);
+        if (e != hipSuccess) { release(c); return map_hip(e); }
+    }
+
+    e = alloc.next_fails() ? hipErrorOutOfMemory
+                           : hipStreamCreateWithFlags(&c->capture_stream, hipStreamNonBlocking);
+    if (e != hipSuccess) { c->capture_stream = nullptr; release(c); return map_hip(e); }
+
+    int khz = 0;
+    e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, cfg->device);
+    if (e != hipSuccess || khz <= 0) { release(c); return KVPUB_ERR_HIP; }
+    const uint64_t ns = cfg->fence_timeout_ns ? cfg->fence_timeout_ns : kDefaultTimeoutNs;
+    c->timeout_ticks = (uint64_t)((double)ns * (double)khz / 1.0e6);
+    if (c->timeout_ticks == 0) c->timeout_ticks = 1;
+
+    *out = c;
+    return KVPUB_OK;
+}
+
+KVPUB_API kvpub_status kvpub_store(kvpub_ctx* ctx, uint32_t layer, int64_t num_tokens,
+                                  const void* latent, int64_t latent_row_stride, const void* rope,
+                                  int64_t rope_row_stride, const void* indexer,
+                                  int64_t indexer_row_stride, const int64_t* slot_mapping,
+                                  kvpub_stream_t stream) {
+    kvpub_status st = check_store(ctx, layer, num_tokens, latent, latent_row_stride, rope,
+                                  rope_row_stride, indexer, indexer_row_stride, slot_mapping);
+    if (st != KVPUB_OK || num_tokens == 0) return st;
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    const StoreParams p = store_params(ctx, layer, num_tokens, latent, latent_row_stride, rope,
+                                       rope_row_stride, indexer, indexer_row_stride, slot_mapping);
+    return map_hip(kvpub::launch_store(p, ctx->cfg.num_replicas, static_cast<hipStream_t>(stream)));
+}
+
+KVPUB_API kvpub_status kvpub_fence(kvpub_ctx* ctx, uint32_t lane, kvpub_stream_t stream) {
+    if (!ctx || lane >= ctx->cfg.num_lanes) return KVPUB_ERR_INVALID_ARG;
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    return map_hip(kvpub::launch_fence(fence_params(ctx, lane), static_cast<hipStream_t>(stream)));
+}
+
+KVPUB_API kvpub_status kvpub_graph_create(kvpub_ctx* ctx, const kvpub_layer_io* io, uint32_t n,
+                                         uint32_t lane, kvpub_graph** out) {
+    if (!out) return KVPUB_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!ctx || !io || n == 0 || lane >= ctx->cfg.num_lanes) return KVPUB_ERR_INVALID_ARG;
+    for (uint32_t i = 0; i < n; ++i) {
+        if (io[i].reserved != 0) return KVPUB_ERR_INVALID_ARG;
+        kvpub_status st = check_store(ctx, io[i].layer, io[i].num_tokens, io[i].latent,
+                                      io[i].latent_row_stride, io[i].rope, io[i].rope_row_stride,
+                                      io[i].indexer, io[i].indexer_row_stride, io[i].slot_mapping);
+        if (st != KVPUB_OK) return st;
+    }
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+
+    kvpub_graph* g = new (std::nothrow) kvpub_graph;
+    if (!g) return KVPUB_ERR_OUT_OF_MEMORY;
+    g->ctx = ctx;
+    g->graph = nullptr;
+    g->exec = nullptr;
+
+    hipStream_t s = ctx->capture_stream;
+    hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) { delete g; return map_hip(e); }
+    hipError_t launch_err = hipSuccess;
+    for (uint32_t i = 0; i < n && launch_err == hipSuccess; ++i) {
+        if (io[i].num_tokens > 0) {
+            const StoreParams p = store_params(ctx, io[i].layer, io[i].num_tokens, io[i].latent,
+                                               io[i].latent_row_stride, io[i].rope,
+                                               io[i].rope_row_stride, io[i].indexer,
+                                               io[i].indexer_row_stride, io[i].slot_mapping);
+            launch_err = kvpub::launch_store(p, ctx->cfg.num_replicas, s);
+        }
+        if (launch_err == hipSuccess) launch_err = kvpub::launch_fence(fence_params(ctx, lane), s);
+    }
+    e = hipStreamEndCapture(s, &g->graph);
+    if (launch_err != hipSuccess || e != hipSuccess) {
+        if (g->graph) (void)hipGraphDestroy(g->graph);
+        delete g;
+        return map_hip(launch_err != hipSuccess ? launch_err : e);
+    }
+    e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(g->graph);
+        delete g;
+        return map_hip(e);
+    }
+    *out = g;
+    return KVPUB_OK;
+}
+
+KVPUB_API kvpub_status kvpub_graph_replay(kvpub_graph* g, kvpub_stream_t stream) {
+    if (!g || !g->exec) return KVPUB_ERR_INVALID_ARG;
+    DeviceGuard guard(g->ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    return map_hip(hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)));
+}
+
+KVPUB_API kvpub_status kvpub_graph_destroy(kvpub_graph* g) {
+    if (!g) return KVPUB_OK;
+    kvpub_status st = KVPUB_OK;
+    {
+        DeviceGuard guard(g->ctx->cfg.device);
+        if (g->exec && hipGraphExecDestroy(g->exec) != hipSuccess) st = KVPUB_ERR_HIP;
+        if (g->graph && hipGraphDestroy(g->graph) != hipSuccess) st = KVPUB_ERR_HIP;
+    }
+    delete g;
+    return st;
+}
+
+KVPUB_API kvpub_status kvpub_epoch_read(kvpub_ctx* ctx, uint32_t lane, uint64_t* out) {
+    if (!ctx || !out || lane >= ctx->cfg.num_lanes) return KVPUB_ERR_INVALID_ARG;
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    kvpub_status st = sync_device();
+    if (st != KVPUB_OK) return st;
+    return map_hip(hipMemcpy(out, epoch_ptr(ctx, lane), sizeof(uint64_t), hipMemcpyDeviceToHost));
+}
+
+KVPUB_API kvpub_status kvpub_error_read(kvpub_ctx* ctx, uint64_t* invalid_slots, uint32_t* flags,
+                                       int clear) {
+    if (!ctx) return KVPUB_ERR_INVALID_ARG;
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    kvpub_status st = sync_device();
+    if (st != KVPUB_OK) return st;
+    uint32_t status = 0;
+    uint64_t invalid = 0;
+    hipError_t e = hipMemcpy(&status, ctx->words + kvpub::kStatusOffset, sizeof status,
+                             hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+        e = hipMemcpy(&invalid, ctx->words + kvpub::kInvalidOffset, sizeof invalid,
+                      hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) e = hipMemset(ctx->words + kvpub::kInvalidOffset, 0, sizeof invalid);
+    if (e == hipSuccess && clear) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return map_hip(e);
+    if (invalid_slots) *invalid_slots = invalid;
+    if (flags) *flags = status;
+    return (status & kvpub::kStatusFenceTimeout) ? KVPUB_ERR_FENCE_TIMEOUT : KVPUB_OK;
+}
+
+KVPUB_API kvpub_status kvpub_participant_signal(kvpub_ctx* ctx, uint32_t lane, uint32_t p,
+                                               volatile uint64_t** out) {
+    if (!ctx || !out || lane >= ctx->cfg.num_lanes) return KVPUB_ERR_INVALID_ARG;
+    if (ctx->cfg.num_participants < 2 || p < 1 || p >= ctx->cfg.num_participants)
+        return KVPUB_ERR_INVALID_ARG;
+    *out = ctx->host_signals + ((size_t)lane * ctx->cfg.num_participants + p) * kvpub::kSignalStride;
+    return KVPUB_OK;
+}
+
+KVPUB_API kvpub_status kvpub_destroy(kvpub_ctx* ctx) {
+    if (!ctx) return KVPUB_OK;
+    kvpub_status st;
+    {
+        DeviceGuard guard(ctx->cfg.device);
+        st = sync_device();
+        release(ctx);
+    }
+    return st;
+}
+
+KVPUB_API const char* kvpub_strerror(kvpub_status s) {
+    switch (s) {
+        case KVPUB_OK: return "ok";
+        case KVPUB_ERR_INVALID_ARG: return "invalid argument";
+        case KVPUB_ERR_OUT_OF_MEMORY: return "out of memory";
+        case KVPUB_ERR_UNSUPPORTED: return "unsupported device (needs gfx950)";
+        case KVPUB_ERR_HIP: return "HIP runtime error";
+        case KVPUB_ERR_CAPTURING: return "synchronizing call during stream capture";
+        case KVPUB_ERR_FENCE_TIMEOUT: return "fence timed out; context poisoned";
+    }
+    return "unknown status";
+}
+
+KVPUB_API uint32_t kvpub_abi_version(void) { return KVPUB_ABI_VERSION; }
+
+}  // extern "C"

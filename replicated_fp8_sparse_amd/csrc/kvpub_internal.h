@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvpub {
+
+constexpr int kMaxReplicas = 8;
+constexpr int kTokensPerWave = 4;     // 4 tokens x 5 tiles = 5 rounds of 4 tiles per wave
+constexpr int kWavesPerBlock = 4;     // 256 threads, 16 tokens per block
+constexpr int kTokensPerBlock = kTokensPerWave * kWavesPerBlock;
+
+constexpr uint32_t kStatusFenceTimeout = 0x1u;
+constexpr uint32_t kStatusPoisoned = 0x2u;
+
+// Words of a context that live in device memory, each on its own 128-byte line.
+constexpr size_t kLine = 128;
+constexpr size_t kStatusOffset = 0;
+constexpr size_t kInvalidOffset = kLine;
+constexpr size_t kEpochOffset = 2 * kLine;          // + lane * kLine
+constexpr size_t kSignalStride = kLine / 8;         // uint64 words between participant signals
+
+struct StoreParams {
+    const uint16_t* latent;      // bf16 bit patterns
+    const uint16_t* rope;
+    const uint16_t* indexer;
+    int64_t latent_stride;       // elements
+    int64_t rope_stride;
+    int64_t indexer_stride;
+    const int64_t* slots;
+    int64_t num_tokens;
+    int64_t capacity;            // num_pages * 64
+    uint64_t main_page_stride;   // bytes
+    uint64_t idx_page_stride;
+    uint8_t* main_base[kMaxReplicas];  // replica r, already offset to the layer
+    uint8_t* idx_base[kMaxReplicas];
+    unsigned long long* invalid_count;
+    const uint32_t* status;
+};
+
+struct FenceParams {
+    uint64_t* epoch;             // this lane's epoch word
+    uint64_t* signals;           // this lane's participant signals, kSignalStride apart
+    uint32_t num_participants;
+    uint32_t self;               // this GPU's participant index (0)
+    uint32_t* status;
+    uint64_t timeout_ticks;      // in wall-clock (s_memrealtime) ticks
+};
+
+// Enqueue one store kernel on `stream`; returns the launch status.
+hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream);
+// Enqueue one fence kernel on `stream`.
+hipError_t launch_fence(const FenceParams& p, hipStream_t stream);
+
+}  // namespace kvpub

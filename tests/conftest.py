@@ -16,3 +16,10 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.get()
+
+
+def pytest_sessionstart(session):
+    # Build the library only if nothing is built yet (build() always rebuilds).
+    from replicated_fp8_sparse_amd import build, kvpub
+    if not os.path.exists(kvpub.LIB_PATH):
+        build.build_library()

@@ -1,0 +1,88 @@
+"""The C-ABI library loads and exports every function include/kvpub.h declares;
+host-side argument checks; the product path has no CPU fallback.  No GPU
+compute is run here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from replicated_fp8_sparse_amd import kvpub
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvpub.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"KVPUB_API\s+[\w\s\*]+?\b(kvpub_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(kvpub.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvpub.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", kvpub.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvpub_\w+)", out))
+    assert exported == set(declared_functions())
+
+
+def test_struct_layouts_match_the_header():
+    cfg = kvpub.kvpub_config_init(2, 3, 100)
+    assert cfg.struct_size == ctypes.sizeof(kvpub.kvpub_config) == 80
+    assert (cfg.num_replicas, cfg.num_layers, cfg.block_size, cfg.num_pages) == (2, 3, 64, 100)
+    assert cfg.main_page_stride == 41984 and cfg.idx_page_stride == 8448
+    assert cfg.main_layer_stride == 100 * 41984 and cfg.idx_layer_stride == 100 * 8448
+    assert ctypes.sizeof(kvpub.kvpub_layer_io) == 72
+    assert kvpub.kvpub_abi_version() == 1
+
+
+def test_strerror_covers_every_status():
+    for st in range(7):
+        assert kvpub.kvpub_strerror(st) not in ("unknown status", "")
+    assert kvpub.kvpub_strerror(99) == "unknown status"
+
+
+def test_host_side_argument_checks():
+    cfg = kvpub.kvpub_config_init(2, 1, 4)
+    cfg.num_replicas = 0
+    st, ctx = kvpub.kvpub_create(cfg, [16, 32], [16, 32])
+    assert st == kvpub.KVPUB_ERR_INVALID_ARG and ctx is None
+    cfg = kvpub.kvpub_config_init(2, 1, 4)
+    st, ctx = kvpub.kvpub_create(cfg, [16, 0], [16, 32])          # null base
+    assert st == kvpub.KVPUB_ERR_INVALID_ARG
+    st, ctx = kvpub.kvpub_create(cfg, [16, 40], [16, 32])         # misaligned base
+    assert st == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_store(None, 0, 4, 16, 512, 16, 64, 16, 128, 16, 0) == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_fence(None, 0, 0) == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_graph_replay(None, 0) == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_graph_destroy(None) == kvpub.KVPUB_OK
+    assert kvpub.kvpub_destroy(None) == kvpub.KVPUB_OK
+    st, _ = kvpub.kvpub_epoch_read(None, 0)
+    assert st == kvpub.KVPUB_ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = kvpub._lib
+    kvpub._lib = None
+    try:
+        with pytest.raises(ImportError):
+            kvpub.load(str(tmp_path / "libkvpub.so"))
+    finally:
+        kvpub._lib = saved
+
+
+def test_product_code_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "replicated_fp8_sparse_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "kvpub_oracle" not in text and "kvo_" not in text, f

@@ -1,0 +1,243 @@
+"""GPU tests of the fence, lanes, host-driven peers, graph capture and replay,
+and context lifetime -- all through the C ABI."""
+import os
+import threading
+import time
+
+import numpy as np
+import pytest
+
+from replicated_fp8_sparse_amd import kvpub, workloads as W
+from replicated_fp8_sparse_amd.workloads import CacheLayout
+
+import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    kvpub.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def test_decode_61_layers_eager(orc):
+    """61 x (store layer l, fence): epoch +61, every layer byte-exact, replicas identical."""
+    layout, xs = W.decode()
+    G.log(f"decode eager: 61 layers T=64 R=2 pages={layout.num_pages}")
+    dev = G.DeviceCache(layout)
+    try:
+        dxs = [G.DeviceInputs(x) for x in xs]
+        for l, dx in enumerate(dxs):
+            kvpub.check(dev.store(l, dx), "kvpub_store")
+            kvpub.check(dev.fence(0), "kvpub_fence")
+        assert dev.epoch(0) == orc_epoch(orc, 0, 61)
+        st, invalid, flags = dev.errors()
+        assert st == kvpub.KVPUB_OK and invalid == 0 and flags == 0
+        for l, x in enumerate(xs):
+            rows = orc.encode_rows(x.latent, x.rope, x.indexer)
+            G.assert_gathered_parity(dev, l, x, rows, "decode")
+        G.assert_replicas_identical(dev)
+        G.log("decode eager: untouched bytes")
+        G.assert_untouched(dev, [(l, x.slots) for l, x in enumerate(xs)])
+    finally:
+        dev.free()
+
+
+def orc_epoch(orc, e0, n):
+    return orc.epoch_after(e0, n)
+
+
+def test_lanes_advance_independently():
+    import torch
+    layout = CacheLayout(replicas=1, layers=1, num_pages=1)
+    dev = G.DeviceCache(layout, lanes=3)
+    try:
+        G.log("lanes: 10 fences on lane 0 (stream A), 7 on lane 2 (stream B)")
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        for _ in range(10):
+            kvpub.check(dev.fence(0, a))
+        for _ in range(7):
+            kvpub.check(dev.fence(2, b))
+        torch.cuda.synchronize()
+        assert (dev.epoch(0), dev.epoch(1), dev.epoch(2)) == (10, 0, 7)
+    finally:
+        dev.free()
+
+
+def test_host_peer_released_fences_complete():
+    """Two participants; the second is a host thread that publishes epochs late."""
+    import torch
+    layout = CacheLayout(replicas=1, layers=1, num_pages=1)
+    dev = G.DeviceCache(layout, participants=2, timeout_ns=5_000_000_000)
+    try:
+        st, sig = kvpub.kvpub_participant_signal(dev.ctx, 0, 1)
+        kvpub.check(st)
+        G.log("host peer: 5 fences, peer publishes 1..5 with 20 ms gaps")
+        for _ in range(5):
+            kvpub.check(dev.fence(0))
+
+        def peer():
+            for k in range(1, 6):
+                time.sleep(0.02)
+                sig[0] = k
+
+        th = threading.Thread(target=peer)
+        th.start()
+        torch.cuda.synchronize()
+        th.join()
+        assert dev.epoch(0) == 5
+        st, _, flags = dev.errors()
+        assert st == kvpub.KVPUB_OK and flags == 0
+    finally:
+        dev.free()
+
+
+def test_fence_timeout_fails_closed(orc):
+    """A peer that never publishes: the bounded wait gives up, the context is
+    poisoned, and later stores write nothing (the kernels all exit normally)."""
+    layout, x = W.tiny()
+    dev = G.DeviceCache(layout, participants=2, timeout_ns=2_000_000)
+    try:
+        G.log("fence timeout: peer never signals, 2 ms limit")
+        kvpub.check(dev.fence(0))
+        st, invalid, flags = dev.errors()
+        assert st == kvpub.KVPUB_ERR_FENCE_TIMEOUT
+        assert flags == kvpub.KVPUB_FLAG_FENCE_TIMEOUT | kvpub.KVPUB_FLAG_POISONED
+        before = dev.host()
+        kvpub.check(dev.store(0, G.DeviceInputs(x)), "kvpub_store")
+        kvpub.check(dev.fence(0))
+        after = dev.host()
+        for a, b in zip(before[0] + before[1], after[0] + after[1]):
+            assert np.array_equal(a, b), "a poisoned context still wrote"
+        assert dev.epoch(0) == 1, "a poisoned fence advanced the epoch"
+    finally:
+        dev.free()
+
+
+def test_graph_replay_61_layers_x100(orc):
+    """Capture 61 x (store, fence) once; replay 100 times with new inputs each time.
+    The epoch reaches 6100, replicas stay identical after every replay, and
+    replays 0 and 99 match the oracle on every written byte."""
+    import torch
+    layout = W.graph_layout()
+    L, T = W.GRAPH_LAYERS, W.GRAPH_T
+    slots = W.graph_slots()
+    G.log(f"graph: {L} layers x T={T}, R=2, pages={layout.num_pages}, 100 replays")
+    dev = G.DeviceCache(layout)
+    graph = None
+    try:
+        lat = torch.empty((L, T, 512), dtype=torch.bfloat16, device="cuda")
+        rope = torch.empty((L, T, 64), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((L, T, 128), dtype=torch.bfloat16, device="cuda")
+        dslots = G.to_dev_i64(slots)
+        ios = [kvpub.layer_io(lat[l].data_ptr(), rope[l].data_ptr(), idx[l].data_ptr(),
+                              dslots.data_ptr(), T, l) for l in range(L)]
+        st, graph = kvpub.kvpub_graph_create(dev.ctx, ios, 0)
+        kvpub.check(st, "kvpub_graph_create")
+        assert dev.epoch(0) == 0, "capturing must not execute anything"
+        stream = torch.cuda.current_stream()
+        for rep in range(100):
+            W.graph_fill_inputs_device(lat, rope, idx, seed=5, replay=rep)
+            kvpub.check(kvpub.kvpub_graph_replay(graph, stream.cuda_stream), "kvpub_graph_replay")
+            torch.cuda.synchronize()
+            G.assert_replicas_identical(dev)
+            if rep in (0, 99):
+                G.log(f"graph: oracle check of replay {rep}")
+                hl = lat.view(torch.int16).cpu().numpy().view(np.uint16)
+                hr = rope.view(torch.int16).cpu().numpy().view(np.uint16)
+                hi = idx.view(torch.int16).cpu().numpy().view(np.uint16)
+                for l in range(L):
+                    x = W.LayerInputs(hl[l], hr[l], hi[l], slots)
+                    rows = G.oracle_rows_parallel(orc, x)
+                    G.assert_gathered_parity(dev, l, x, rows, f"graph replay {rep}")
+        assert dev.epoch(0) == orc.epoch_after(0, L * 100)
+        st, invalid, flags = dev.errors()
+        assert st == kvpub.KVPUB_OK and invalid == 0 and flags == 0
+        G.log("graph: untouched bytes")
+        G.assert_untouched(dev, [(l, slots) for l in range(L)])
+    finally:
+        if graph is not None:
+            kvpub.kvpub_graph_destroy(graph)
+        dev.free()
+
+
+def test_store_and_fence_under_torch_graph_capture(orc):
+    """kvpub_store and kvpub_fence are capture-safe inside an external torch CUDA graph."""
+    import torch
+    layout, x = W.tiny()
+    dev = G.DeviceCache(layout)
+    try:
+        G.log("torch graph capture of store + fence, 5 replays")
+        dx = G.DeviceInputs(x)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                kvpub.check(dev.store(0, dx, stream=s), "kvpub_store (capture)")
+                kvpub.check(dev.fence(0, stream=s), "kvpub_fence (capture)")
+        torch.cuda.synchronize()
+        assert dev.epoch(0) == 0
+        for i in range(5):
+            g.replay()
+            torch.cuda.synchronize()
+            assert dev.epoch(0) == i + 1
+        mains, idxs, _ = G.oracle_replicas(orc, layout, [(0, x)])
+        G.assert_full_parity(dev, mains, idxs)
+        del g
+    finally:
+        dev.free()
+
+
+@pytest.mark.parametrize("fail_at", [1, 2, 3])
+def test_create_is_all_or_nothing(fail_at):
+    import torch
+    layout = CacheLayout(replicas=2, layers=1, num_pages=2)
+    dev = G.DeviceCache(layout, create=False)
+    try:
+        G.log(f"allocation failure injected at allocation {fail_at}")
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        os.environ["KVPUB_TEST_FAIL_ALLOC_AT"] = str(fail_at)
+        try:
+            st, ctx = dev.create(participants=2)
+        finally:
+            del os.environ["KVPUB_TEST_FAIL_ALLOC_AT"]
+        assert st == kvpub.KVPUB_ERR_OUT_OF_MEMORY and ctx is None
+        assert torch.cuda.mem_get_info()[0] == free0
+        st, ctx = dev.create(participants=2)
+        kvpub.check(st)
+        dev.ctx = ctx
+    finally:
+        dev.free()
+
+
+def test_create_rejects_bad_config():
+    layout = CacheLayout(replicas=2, layers=2, num_pages=4)
+    dev = G.DeviceCache(layout, create=False)
+    try:
+        G.log("bad configs")
+        mb = [b.data_ptr() for b in dev.main]
+        ib = [b.data_ptr() for b in dev.idx]
+        for field, val in (("num_replicas", 0), ("num_replicas", 9), ("block_size", 32),
+                           ("main_page_stride", 41983), ("idx_page_stride", 8440),
+                           ("main_layer_stride", 3 * 41984), ("num_lanes", 0),
+                           ("num_lanes", 65), ("num_participants", 9), ("flags", 1),
+                           ("struct_size", 8)):
+            cfg = dev.config()
+            setattr(cfg, field, val)
+            st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+            assert st == kvpub.KVPUB_ERR_INVALID_ARG and ctx is None, (field, val, st)
+        st, ctx = kvpub.kvpub_create(dev.config(), [mb[0] + 8, mb[1]], ib)
+        assert st == kvpub.KVPUB_ERR_INVALID_ARG
+        cfg = dev.config()
+        cfg.device = 64
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        assert st == kvpub.KVPUB_ERR_INVALID_ARG
+    finally:
+        dev.free()

@@ -1,0 +1,247 @@
+"""GPU parity of kvpub_store against the CPU oracle, byte for byte.
+
+Every test calls the HIP path through the C ABI (libkvpub.so) and compares
+every byte of every replica with the oracle run on the same input bytes.
+Small cases compare whole buffers; the full-size prefill and heavy-tail
+workloads compare every written row (gathered on the GPU) and check on the
+GPU that every other byte still holds the fill / guard pattern.
+"""
+import numpy as np
+import pytest
+
+from replicated_fp8_sparse_amd import kvpub, workloads as W
+from replicated_fp8_sparse_amd.workloads import CacheLayout, LayerInputs, bf16_bits
+
+import gpu_util as G
+import pins
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on CPU-only machines)")
+    kvpub.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def run_full(orc, layout, layer_inputs, label):
+    """Store [(layer, LayerInputs)] on the GPU and compare whole buffers with the oracle."""
+    G.log(f"{label}: R={layout.replicas} pages={layout.num_pages} layers={layout.layers}")
+    dev = G.DeviceCache(layout)
+    try:
+        for layer, x in layer_inputs:
+            dx = G.DeviceInputs(x)
+            kvpub.check(dev.store(layer, dx), "kvpub_store")
+        st, invalid, flags = dev.errors()
+        kvpub.check(st, "kvpub_error_read")
+        mains, idxs, want_invalid = G.oracle_replicas(orc, layout, layer_inputs)
+        G.assert_full_parity(dev, mains, idxs)
+        assert invalid == want_invalid, f"invalid slots {invalid} != {want_invalid}"
+        assert flags == 0
+    finally:
+        dev.free()
+
+
+def test_tiny_parity(orc):
+    layout, x = W.tiny()
+    run_full(orc, layout, [(0, x)], "tiny T=256")
+
+
+def _hand_rows(rng):
+    """Tokens that reach the corners of the quantizer."""
+    rows = []
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+
+    def token(lat, idx):
+        rows.append((lat.astype(np.uint16), idx.astype(np.uint16)))
+
+    # e4m3-exact tiles with amax 448 (scale exactly 1.0) and the same pattern x 2^k
+    for k in (0, -20, 20):
+        codes = rng.choice(finite, size=640)
+        codes[::128] = 0x7E
+        vals = pins.e4m3_decode(codes) * 2.0 ** k
+        b = bf16_bits(vals.astype(np.float32))
+        token(b[:512], b[512:])
+    # smallest bf16 subnormal as amax (the scale is a binary32 subnormal)
+    b = np.zeros(640, np.uint16)
+    b[rng.choice(640, 100, replace=False)] = 0x0001
+    b[rng.choice(640, 100, replace=False)] = 0x8001
+    b[rng.choice(640, 50, replace=False)] = 0x8000
+    b[0::128] = 0x0001
+    token(b[:512], b[512:])
+    # -0.0 inside non-zero tiles, alternating signs, all elements equal to amax
+    b = bf16_bits(rng.standard_normal(640).astype(np.float32))
+    b[1::3] = 0x8000
+    token(b[:512], b[512:])
+    b = bf16_bits((np.where(np.arange(640) % 2, -1.0, 1.0) * 3.25).astype(np.float32))
+    token(b[:512], b[512:])
+    # tiles far below / around the fast-division threshold, and near the bf16 maximum
+    for mag in (1e-20, 448.0 * 2.0 ** -64, 448.0 * 2.0 ** -64 * (1 - 2 ** -8), 1e-37, 1e30, 3.0e38):
+        v = rng.standard_normal(640)
+        v = v / np.abs(v).max() * mag
+        token(bf16_bits(v[:512].astype(np.float32)), bf16_bits(v[512:].astype(np.float32)))
+    b = np.full(640, 0x7F7F, np.uint16)
+    b[1::2] = 0xFF7F
+    token(b[:512], b[512:])
+    # one element per tile much larger than the rest (the other codes underflow)
+    v = rng.standard_normal(640) * 1e-3
+    v[::128] = 1e4
+    token(bf16_bits(v[:512].astype(np.float32)), bf16_bits(v[512:].astype(np.float32)))
+    return rows
+
+
+def test_hand_cases_parity(orc):
+    rng = np.random.default_rng(101)
+    rows = _hand_rows(rng)
+    n = len(rows)
+    layout = CacheLayout(replicas=2, layers=2, num_pages=16, guard=64)
+    T = n + 8
+    latent = bf16_bits(rng.standard_normal((T, 512)).astype(np.float32))
+    rope = rng.integers(0, 65536, size=(T, 64), dtype=np.uint16)   # any bit pattern passes through
+    indexer = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32))
+    for t, (lat, idx) in enumerate(rows):
+        latent[t], indexer[t] = lat, idx
+    slots = rng.permutation(layout.capacity)[:T].astype(np.int64)
+    # 3 slots >= capacity, one negative invalid slot, padded tokens
+    slots[n + 0] = layout.capacity
+    slots[n + 1] = layout.capacity + 12345
+    slots[n + 2] = 2 ** 40
+    slots[n + 3] = -7
+    slots[n + 4:] = -1
+    run_full(orc, layout, [(1, LayerInputs(latent, rope, indexer, slots))], f"hand cases T={T}")
+
+
+def test_encoder_sweep_parity(orc):
+    """Tiles with amax 448 have scale 1.0, so every bf16 value in [-448, 448] is
+    fed to the e4m3 conversion exactly once."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = pins.bf16_to_f32(b)
+    vals = b[np.isfinite(v) & (np.abs(v) <= 448.0)]
+    per_tile = 127
+    n_tiles = -(-vals.size // per_tile)
+    tiles = np.zeros((n_tiles, 128), np.uint16)
+    flat = np.zeros(n_tiles * per_tile, np.uint16)
+    flat[:vals.size] = vals
+    tiles[:, :per_tile] = flat.reshape(n_tiles, per_tile)
+    tiles[:, per_tile] = 0x43E0  # 448.0
+    n_tok = -(-n_tiles // 5)
+    allt = np.zeros((n_tok * 5, 128), np.uint16)
+    allt[:n_tiles] = tiles
+    allt[n_tiles:, 0] = 0x43E0
+    allt = allt.reshape(n_tok, 5, 128)
+    latent = allt[:, :4].reshape(n_tok, 512)
+    indexer = allt[:, 4].copy()
+    rng = np.random.default_rng(102)
+    rope = rng.integers(0, 65536, size=(n_tok, 64), dtype=np.uint16)
+    layout = CacheLayout(replicas=1, layers=1, num_pages=4)
+    slots = rng.permutation(layout.capacity)[:n_tok].astype(np.int64)
+    run_full(orc, layout, [(0, LayerInputs(latent, rope, indexer, slots))], f"encoder sweep T={n_tok}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 7, 13, 17, 31, 33, 63, 65, 100, 1001])
+def test_ragged_and_strided(orc, T):
+    """Token counts that leave partial waves and blocks; inputs with row strides
+    wider than the rows; three replicas."""
+    import torch
+    rng = np.random.default_rng(200 + T)
+    layout = CacheLayout(replicas=3, layers=1, num_pages=32)
+    LS, RS, IS = 520, 72, 136
+    wide_l = bf16_bits(rng.standard_normal((T, LS)).astype(np.float32))
+    wide_r = bf16_bits(rng.standard_normal((T, RS)).astype(np.float32))
+    wide_i = bf16_bits(rng.standard_normal((T, IS)).astype(np.float32))
+    slots = rng.permutation(layout.capacity)[:T].astype(np.int64)
+    if T > 4:
+        slots[rng.choice(T, T // 5, replace=False)] = -1
+    x = LayerInputs(np.ascontiguousarray(wide_l[:, :512]), np.ascontiguousarray(wide_r[:, :64]),
+                    np.ascontiguousarray(wide_i[:, :128]), slots)
+    G.log(f"ragged T={T} strides {LS}/{RS}/{IS}")
+    dev = G.DeviceCache(layout)
+    try:
+        dl, dr, di = G.to_dev_u16(wide_l), G.to_dev_u16(wide_r), G.to_dev_u16(wide_i)
+        ds = G.to_dev_i64(slots)
+        st = kvpub.kvpub_store(dev.ctx, 0, T, dl.data_ptr(), LS, dr.data_ptr(), RS, di.data_ptr(),
+                               IS, ds.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        kvpub.check(st, "kvpub_store")
+        mains, idxs, _ = G.oracle_replicas(orc, layout, [(0, x)])
+        G.assert_full_parity(dev, mains, idxs)
+    finally:
+        dev.free()
+
+
+def test_empty_store_is_noop(orc):
+    layout = CacheLayout(replicas=2, layers=1, num_pages=2)
+    dev = G.DeviceCache(layout)
+    try:
+        G.log("empty store T=0")
+        before = dev.host()
+        st = kvpub.kvpub_store(dev.ctx, 0, 0, 0, 512, 0, 64, 0, 128, 0, 0)
+        assert st == kvpub.KVPUB_OK
+        after = dev.host()
+        for a, b in zip(before[0] + before[1], after[0] + after[1]):
+            assert np.array_equal(a, b)
+    finally:
+        dev.free()
+
+
+def test_bad_arguments_write_nothing(orc):
+    import torch
+    layout, x = W.tiny()
+    dev = G.DeviceCache(layout)
+    try:
+        G.log("bad arguments")
+        dx = G.DeviceInputs(x)
+        s = torch.cuda.current_stream().cuda_stream
+        p = (dx.latent.data_ptr(), dx.rope.data_ptr(), dx.indexer.data_ptr(), dx.slots.data_ptr())
+        bad = [
+            (dev.ctx, 1, x.slots.size, p[0], 512, p[1], 64, p[2], 128, p[3], s),      # layer >= L
+            (dev.ctx, 0, -1, p[0], 512, p[1], 64, p[2], 128, p[3], s),                # T < 0
+            (dev.ctx, 0, 16, p[0] + 2, 512, p[1], 64, p[2], 128, p[3], s),            # misaligned
+            (dev.ctx, 0, 16, p[0], 511, p[1], 64, p[2], 128, p[3], s),                # stride < row
+            (dev.ctx, 0, 16, p[0], 516, p[1], 64, p[2], 128, p[3], s),                # stride % 8
+            (dev.ctx, 0, 16, p[0], 512, p[1], 64, p[2], 128, 0, s),                   # null slots
+            (None, 0, 16, p[0], 512, p[1], 64, p[2], 128, p[3], s),                   # null ctx
+        ]
+        before = dev.host()
+        for args in bad:
+            assert kvpub.kvpub_store(*args) == kvpub.KVPUB_ERR_INVALID_ARG, args
+        assert kvpub.kvpub_fence(dev.ctx, 1, s) == kvpub.KVPUB_ERR_INVALID_ARG
+        after = dev.host()
+        for a, b in zip(before[0] + before[1], after[0] + after[1]):
+            assert np.array_equal(a, b)
+        assert dev.epoch(0) == 0
+    finally:
+        dev.free()
+
+
+def _big_parity(orc, layout, x, label):
+    G.log(f"{label}: T={x.slots.size} R={layout.replicas} pages={layout.num_pages}")
+    dev = G.DeviceCache(layout)
+    try:
+        dx = G.DeviceInputs(x)
+        kvpub.check(dev.store(0, dx), "kvpub_store")
+        st, invalid, flags = dev.errors()
+        kvpub.check(st, "kvpub_error_read")
+        assert invalid == 0 and flags == 0
+        G.log(f"{label}: oracle rows")
+        rows = G.oracle_rows_parallel(orc, x)
+        G.log(f"{label}: compare written rows")
+        G.assert_gathered_parity(dev, 0, x, rows, label)
+        G.assert_replicas_identical(dev)
+        G.log(f"{label}: untouched bytes")
+        G.assert_untouched(dev, [(0, x.slots)])
+    finally:
+        dev.free()
+
+
+def test_prefill_full_size(orc):
+    layout, x = W.prefill()
+    _big_parity(orc, layout, x, "prefill")
+
+
+def test_heavy_full_size(orc):
+    layout, x = W.heavy()
+    _big_parity(orc, layout, x, "heavy-tail")
