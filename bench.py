@@ -31,6 +31,22 @@ READ_BYTES_PER_TOKEN = (512 + 64 + 128) * 2         # bf16 rows read
 WRITE_BYTES_PER_TOKEN_PER_REPLICA = 656 + 128 + 4   # Main-KV row + Indexer-K codes + scale
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "store_kernel_graph_T4096_R2_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "replicated_fp8_sparse_amd", "csrc", "store_kernel.hip")
+
+
+def measured_traffic():
+    """HBM bytes per store launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record (scaled by a 256 MiB copy), or None if the kernel source changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == src else None
+
+
 def alg_bytes(valid_tokens, replicas):
     return valid_tokens * (READ_BYTES_PER_TOKEN + replicas * WRITE_BYTES_PER_TOKEN_PER_REPLICA)
 
@@ -45,6 +61,9 @@ def parse():
                     help="skip the prefill / heavy-tail store-only figures")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (torch copy_) three times, so that "
+                         "memory-traffic counters can be scaled by a kernel of known size")
     return ap.parse_args()
 
 
@@ -80,8 +99,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         sys.exit(2)
-    lib = kvpub.load()
+    kvpub.load()
     dev_name = torch.cuda.get_device_name(0)
+    if args.pmc_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     L, T = W.GRAPH_LAYERS, W.GRAPH_T
     layout = W.graph_layout()
@@ -137,11 +164,12 @@ def main():
                 kvpub.check(kvpub.kvpub_store(ctx, l, T, lat[l].data_ptr(), 512, rope[l].data_ptr(), 64,
                                               idx[l].data_ptr(), 128, slots.data_ptr(), sh))
     reps = max(4, args.steps // 4)
-    for _ in range(2):
-        g_store.replay()
-    with Timer(torch, stream) as ts:
-        for _ in range(reps):
+    with torch.cuda.stream(stream):
+        for _ in range(2):
             g_store.replay()
+        with Timer(torch, stream) as ts:
+            for _ in range(reps):
+                g_store.replay()
     store_us = ts.ms * 1e3 / (reps * L)
     store_bytes = alg_bytes(valid, R)
     store_gbps = store_bytes / (store_us * 1e-6) / 1e9
@@ -152,11 +180,12 @@ def main():
         with torch.cuda.graph(g_fence, stream=stream):
             for l in range(L):
                 kvpub.check(kvpub.kvpub_fence(ctx, 0, sh))
-    for _ in range(2):
-        g_fence.replay()
-    with Timer(torch, stream) as tf:
-        for _ in range(reps):
+    with torch.cuda.stream(stream):
+        for _ in range(2):
             g_fence.replay()
+        with Timer(torch, stream) as tf:
+            for _ in range(reps):
+                g_fence.replay()
     fence_us_alone = tf.ms * 1e3 / (reps * L)
     fence_us_in_step = (step_ms * 1e3 - store_us * L) / L
     st, invalid, flags = kvpub.kvpub_error_read(ctx, False)
@@ -195,7 +224,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(store_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, scaled by a 256 MiB copy)",
             "alg_bytes_per_launch": store_bytes,
             "avg_launch_us": round(store_us, 3),
             "how": "HIP events around replays of a graph of the 61 store launches alone",

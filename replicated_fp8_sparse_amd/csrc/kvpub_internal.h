@@ -8,7 +8,10 @@ namespace kvpub {
 
 constexpr int kMaxReplicas = 8;
 constexpr int kTokensPerWave = 4;     // 4 tokens x 5 tiles = 5 rounds of 4 tiles per wave
-constexpr int kWavesPerBlock = 4;     // 256 threads, 16 tokens per block
+#ifndef KVPUB_WPB
+#define KVPUB_WPB 4
+#endif
+constexpr int kWavesPerBlock = KVPUB_WPB;     // 256 threads, 16 tokens per block
 constexpr int kTokensPerBlock = kTokensPerWave * kWavesPerBlock;
 
 constexpr uint32_t kStatusFenceTimeout = 0x1u;
@@ -37,6 +40,8 @@ struct StoreParams {
     uint8_t* idx_base[kMaxReplicas];
     unsigned long long* invalid_count;
     const uint32_t* status;
+    int32_t num_cus;             // compute units of the device (sets the grid)
+    int64_t groups_per_wave;     // set by launch_store
 };
 
 struct FenceParams {

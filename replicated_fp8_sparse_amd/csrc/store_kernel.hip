@@ -7,15 +7,17 @@
 // diagram replaces the gather + receive-side insert with stores to each cache.
 // Here the R replicas are R buffers in this GPU's HBM.
 //
-// Work mapping (wave64).  A wave owns 4 consecutive tokens.  A token has five
-// 128-element tiles (4 latent + 1 indexer); a DPP row of 16 lanes x 8 bf16
-// (one 16-byte load per lane) is exactly one tile, so one wave instruction
-// covers 4 tiles and the 20 tiles of 4 tokens take 5 rounds with every lane
-// busy:
+// Work mapping (wave64).  A wave owns a group of 4 consecutive tokens.  A
+// token has five 128-element tiles (4 latent + 1 indexer); a DPP row of 16
+// lanes x 8 bf16 (one 16-byte load per lane) is exactly one tile, so one wave
+// instruction covers 4 tiles and the 20 tiles of a group take 5 rounds with
+// every lane busy:
 //   round k = 0..3: token k's latent, lanes 16j..16j+15 = tile j;
 //   round 4:        the indexer rows, lanes 16g..16g+15 = token g.
 // Lanes 0..31 also carry the 4 tokens' RoPE rows (8 lanes x 16 B each), which
-// are copied through unchanged.  Every input byte is loaded once, up front.
+// are copied through unchanged.  Every input byte is loaded once, up front,
+// with token indices clamped to the last token so no load waits on a branch
+// or on the slot values.
 //
 // Per tile: amax from the bf16 magnitude bits (packed u16 max in-lane, then a
 // 4-step DPP max within the row), scale = amax / 448 (IEEE binary32
@@ -29,7 +31,9 @@
 // (round-to-nearest-even); |x/scale| < 450 for finite input, below the
 // saturation boundary at 464, and quotients are clamped to 448 first.
 //
-// Stores are non-temporal: the cache rows are not re-read by this kernel.
+// Every piece is stored straight to its slot in each replica (ordinary
+// write-back stores, so neighbouring pieces of a 128-byte line merge in L2);
+// the inputs are read with non-temporal loads (read once, never reused).
 #include "kvpub_internal.h"
 
 namespace kvpub {
@@ -131,106 +135,166 @@ __device__ __forceinline__ u32x2 quant8(u32x4 d, const TileScale& t) {
     return u32x2{(uint32_t)w0, (uint32_t)w1};
 }
 
-template <typename T>
-__device__ __forceinline__ void store_nt(uint8_t* p, T v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<T*>(p));
+
+#ifndef KVPUB_XCD
+#define KVPUB_XCD 1
+#endif
+#ifndef KVPUB_WPC
+#define KVPUB_WPC 16   // target waves per CU before a block takes several block-groups
+#endif
+
+// One group = 4 consecutive tokens: their rows (loaded once) and slots.
+struct Group {
+    u32x4 lat[4];    // latent of token k: lane l holds elements 8l..8l+7
+    u32x4 ix;        // indexer of token g = l/16: elements 8(l%16)..+7
+    u32x4 rp;        // RoPE of token (l/8)%4: elements 8(l%8)..+7 (lanes 32..63 repeat 0..31)
+    int64_t s[4];    // wave-uniform slots of the 4 tokens, -1 past the last token
+    int64_t sg;      // slot of this lane's indexer token
+    int64_t sr;      // slot of this lane's RoPE token
+};
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <typename T>
-__device__ __forceinline__ T pick4(const T (&v)[4], uint32_t i) {
-    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+// Issue every load of a group.  Token indices past the end are clamped to the
+// last token (always in bounds) and their slots forced to -1.
+__device__ __forceinline__ void load_group(const StoreParams& p, int64_t t0, uint32_t lane, Group& G) {
+    const int64_t last = p.num_tokens - 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t t = t0 + k < last ? t0 + k : last;
+        G.lat[k] = ld16(p.latent + t * p.latent_stride + lane * 8);
+    }
+    const int64_t ug = t0 + (lane >> 4), ur = t0 + ((lane >> 3) & 3u);
+    const int64_t tg = ug < last ? ug : last, tr = ur < last ? ur : last;
+    G.ix = ld16(p.indexer + tg * p.indexer_stride + (lane & 15u) * 8);
+    G.rp = ld16(p.rope + tr * p.rope_stride + (lane & 7u) * 8);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t t = t0 + k < last ? t0 + k : last;
+        const int64_t v = p.slots[t];
+        G.s[k] = t0 + k <= last ? v : -1;
+    }
+    const int64_t vg = p.slots[tg], vr = p.slots[tr];
+    G.sg = ug <= last ? vg : -1;
+    G.sr = ur <= last ? vr : -1;
 }
 
-template <int R>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(const StoreParams p) {
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t chunk = xcd_chunk(blockIdx.x, gridDim.x);
-    const int64_t t0 = ((int64_t)chunk * kWavesPerBlock + wave) * kTokensPerWave;
-    if (t0 >= p.num_tokens) return;
-    if (*p.status & kStatusPoisoned) return;  // a fence timed out: fail closed
+__device__ __forceinline__ bool slot_ok(int64_t s, int64_t capacity) {
+    return (uint64_t)s < (uint64_t)capacity;   // negative slots wrap to huge values
+}
 
-    // Slots of the wave's tokens (wave-uniform).
-    int64_t slot[4];
-    bool ok[4];
-    uint32_t nbad = 0;
+// Quantize a group and hand every output piece to `out`:
+//   out.codes(k, c)     Main-KV row bytes [8*lane, +8) of token k
+//   out.scales(k, v)    row bytes [512, 528) of token k (lane 0 only)
+//   out.rope(v)         row bytes [528 + 16*(lane%8), +16) of token lane/8 (lanes 0..31)
+//   out.icodes(c)       Indexer-K codes [8*(lane%16), +8) of token lane/16
+//   out.iscale(v)       Indexer-K scale of token lane/16 (lanes 16g only)
+// tok[k] (wave-uniform), ok_r and ok_g (per lane) select what is produced.
+template <class Out>
+__device__ __forceinline__ void quantize_group(const Group& G, uint32_t lane, const bool (&tok)[4],
+                                               bool ok_r, bool ok_g, Out& out) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int64_t t = t0 + k;
-        slot[k] = t < p.num_tokens ? p.slots[t] : -1;
-        ok[k] = slot[k] >= 0 && slot[k] < p.capacity;
-        nbad += (!ok[k] && slot[k] != -1) ? 1u : 0u;
-    }
-    if (nbad != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
-
-    // Issue every load of the wave before any arithmetic.
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 lat[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        lat[k] = zero;
-        if (ok[k])
-            lat[k] = *reinterpret_cast<const u32x4*>(p.latent + (t0 + k) * p.latent_stride + lane * 8);
-    }
-    const uint32_t g = lane >> 4, li = lane & 15u;
-    const bool okg = pick4(ok, g);
-    u32x4 ix = zero;
-    if (okg) ix = *reinterpret_cast<const u32x4*>(p.indexer + (t0 + g) * p.indexer_stride + li * 8);
-    const uint32_t rk = (lane >> 3) & 3u;
-    const bool okr = lane < 32 && pick4(ok, rk);
-    u32x4 rp = zero;
-    if (okr) rp = *reinterpret_cast<const u32x4*>(p.rope + (t0 + rk) * p.rope_stride + (lane & 7u) * 8);
-
-    // Rounds 0..3: latent tiles of token k.
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if (!ok[k]) continue;
-        const TileScale ts = tile_scale(row_max16(lane_amax_bits(lat[k])));
-        const u32x2 codes = quant8(lat[k], ts);
+        if (!tok[k]) continue;
+        const TileScale ts = tile_scale(row_max16(lane_amax_bits(G.lat[k])));
+        out.codes(k, quant8(G.lat[k], ts));
         const uint32_t sb = __float_as_uint(ts.scale);
         const u32x4 scales = {(uint32_t)__builtin_amdgcn_readlane((int)sb, 0),
                               (uint32_t)__builtin_amdgcn_readlane((int)sb, 16),
                               (uint32_t)__builtin_amdgcn_readlane((int)sb, 32),
                               (uint32_t)__builtin_amdgcn_readlane((int)sb, 48)};
-        const uint64_t off = (uint64_t)(slot[k] >> 6) * p.main_page_stride +
-                             (uint64_t)(slot[k] & 63) * 656u;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint8_t* row = p.main_base[r] + off;
-            store_nt(row + lane * 8, codes);
-            if (lane == 0) store_nt(row + 512, scales);
-        }
+        if (lane == 0) out.scales(k, scales);
     }
-
-    // RoPE: lanes 0..31, token rk, 16 bytes each at [528, 656).
-    if (okr) {
-        const int64_t s = pick4(slot, rk);
-        const uint64_t off = (uint64_t)(s >> 6) * p.main_page_stride + (uint64_t)(s & 63) * 656u +
-                             528u + (lane & 7u) * 16u;
-#pragma unroll
-        for (int r = 0; r < R; ++r) store_nt(p.main_base[r] + off, rp);
+    if (lane < 32 && ok_r) out.rope(G.rp);
+    // every row computes its indexer tile (the DPP reduction needs full rows)
+    const TileScale ts = tile_scale(row_max16(lane_amax_bits(G.ix)));
+    const u32x2 codes = quant8(G.ix, ts);
+    if (ok_g) {
+        out.icodes(codes);
+        if ((lane & 15u) == 0) out.iscale(__float_as_uint(ts.scale));
     }
+}
 
-    // Round 4: the indexer row of token g in row g.
-    if (okg) {
-        const TileScale ts = tile_scale(row_max16(lane_amax_bits(ix)));
-        const u32x2 codes = quant8(ix, ts);
-        const int64_t s = pick4(slot, g);
-        const uint64_t page = (uint64_t)(s >> 6) * p.idx_page_stride;
-        const uint64_t o = (uint64_t)(s & 63);
+// Stores each piece at its slot in every replica.
+template <int R>
+struct ScatterOut {
+    const StoreParams& p;
+    const Group& G;
+    uint32_t lane;
+    __device__ uint64_t row_off(int64_t s) const {
+        return (uint64_t)(s >> 6) * p.main_page_stride + (uint64_t)(s & 63) * 656u;
+    }
+    __device__ void codes(int k, u32x2 c) {
+        const uint64_t o = row_off(G.s[k]) + lane * 8u;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint8_t* pg = p.idx_base[r] + page;
-            store_nt(pg + o * 128u + li * 8u, codes);
-            if (li == 0) store_nt(pg + 8192u + o * 4u, __float_as_uint(ts.scale));
+        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x2*>(p.main_base[r] + o) = c;
+    }
+    __device__ void scales(int k, u32x4 v) {
+        const uint64_t o = row_off(G.s[k]) + 512u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(p.main_base[r] + o) = v;
+    }
+    __device__ void rope(u32x4 v) {
+        const uint64_t o = row_off(G.sr) + 528u + (lane & 7u) * 16u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(p.main_base[r] + o) = v;
+    }
+    __device__ void icodes(u32x2 c) {
+        const uint64_t o = (uint64_t)(G.sg >> 6) * p.idx_page_stride + (uint64_t)(G.sg & 63) * 128u +
+                           (lane & 15u) * 8u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x2*>(p.idx_base[r] + o) = c;
+    }
+    __device__ void iscale(uint32_t v) {
+        const uint64_t o = (uint64_t)(G.sg >> 6) * p.idx_page_stride + 8192u + (uint64_t)(G.sg & 63) * 4u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) *reinterpret_cast<uint32_t*>(p.idx_base[r] + o) = v;
+    }
+};
+
+// Each wave owns a contiguous run of p.groups_per_wave groups (4 tokens each);
+// blocks are mapped XCD-aware so that neighbouring groups share an L2.
+template <int R>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(const StoreParams p) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#if KVPUB_XCD
+    const uint32_t chunk = xcd_chunk(blockIdx.x, gridDim.x);
+#else
+    const uint32_t chunk = blockIdx.x;
+#endif
+    const int64_t ngroups = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave;
+    const int64_t g0 = ((int64_t)chunk * kWavesPerBlock + wave) * p.groups_per_wave;
+    const int64_t g1 = g0 + p.groups_per_wave < ngroups ? g0 + p.groups_per_wave : ngroups;
+    for (int64_t g = g0; g < g1; ++g) {
+        Group G;
+        load_group(p, g * kTokensPerWave, lane, G);
+        if (*p.status & kStatusPoisoned) return;  // a fence timed out: fail closed
+        // Invalid (neither -1 nor a slot of the cache) slots are skipped and counted.
+        uint32_t nbad = 0;
+        bool tok[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            tok[k] = slot_ok(G.s[k], p.capacity);
+            nbad += (G.s[k] != -1 && !tok[k]) ? 1u : 0u;
         }
+        if (nbad != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
+        ScatterOut<R> out{p, G, lane};
+        quantize_group(G, lane, tok, slot_ok(G.sr, p.capacity), slot_ok(G.sg, p.capacity), out);
     }
 }
 
 }  // namespace
 
-hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream) {
-    const int64_t blocks = (p.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
+hipError_t launch_store(const StoreParams& p_in, uint32_t num_replicas, hipStream_t stream) {
+    StoreParams p = p_in;
+    const int64_t ngroups = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave;
+    const int64_t max_waves = (int64_t)p.num_cus * KVPUB_WPC;
+    p.groups_per_wave = ngroups <= max_waves ? 1 : (ngroups + max_waves - 1) / max_waves;
+    const int64_t waves = (ngroups + p.groups_per_wave - 1) / p.groups_per_wave;
+    const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 grid((uint32_t)blocks), block(kWavesPerBlock * 64);
     (void)hipGetLastError();
     switch (num_replicas) {

@@ -245,3 +245,37 @@ def test_prefill_full_size(orc):
 def test_heavy_full_size(orc):
     layout, x = W.heavy()
     _big_parity(orc, layout, x, "heavy-tail")
+
+
+def _run_slots(rng, T, capacity, kind):
+    if kind == "from0":
+        return np.arange(T, dtype=np.int64)
+    if kind == "offset3":
+        return 3 + np.arange(T, dtype=np.int64)
+    if kind == "offset61":               # every unit straddles a page boundary somewhere
+        return 61 + np.arange(T, dtype=np.int64)
+    if kind == "reversed":
+        return (T - 1 - np.arange(T, dtype=np.int64))
+    if kind == "holes":                  # runs broken by pads and invalid slots inside units
+        s = 8 + np.arange(T, dtype=np.int64)
+        s[5::23] = -1
+        s[11::37] = capacity + 5
+        return s
+    if kind == "pages":                  # whole pages in random order, tail partial
+        return W.perm_page_slots(rng, T, capacity // 64)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("T", [8, 16, 17, 40, 63, 1000])
+@pytest.mark.parametrize("kind", ["from0", "offset3", "offset61", "reversed", "holes", "pages"])
+def test_consecutive_slot_runs(orc, T, kind):
+    """Slot runs (the row-image path) and broken runs (the piece-by-piece path)
+    in the same launch, two replicas, page guards."""
+    rng = np.random.default_rng(300 + T)
+    layout = CacheLayout(replicas=2, layers=1, num_pages=24, guard=64)
+    slots = _run_slots(rng, T, layout.capacity, kind)
+    latent = bf16_bits(rng.standard_normal((T, 512)).astype(np.float32))
+    rope = bf16_bits(rng.standard_normal((T, 64)).astype(np.float32))
+    indexer = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32))
+    latent[T // 2] = 0                   # an all-zero row inside a run
+    run_full(orc, layout, [(0, LayerInputs(latent, rope, indexer, slots))], f"runs {kind} T={T}")
