@@ -14,9 +14,12 @@ ARCH = "gfx950"
 
 # No fast-math, no FP contraction (explicit fmaf only); packed-fp32 instructions
 # off for every HIP file.
+# Kernel arguments that are plain scalars are preloaded into SGPRs at wave
+# launch (the first 14 dwords: the store kernel's row pointers and strides).
 HIPFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
             "-DKVPUB_BUILD_SHARED", "-ffp-contract=off",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=14",
             "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -123,9 +123,9 @@ kvpub_status check_store(const kvpub_ctx* ctx, uint32_t layer, int64_t T, const 
     if (!latent || !rope || !indexer || !slots) return KVPUB_ERR_INVALID_ARG;
     if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(indexer, 16) || !aligned(slots, 8))
         return KVPUB_ERR_INVALID_ARG;
-    if (ls < (int64_t)KVPUB_LATENT_DIM || ls % 8) return KVPUB_ERR_INVALID_ARG;
-    if (rs < (int64_t)KVPUB_ROPE_DIM || rs % 8) return KVPUB_ERR_INVALID_ARG;
-    if (is < (int64_t)KVPUB_INDEXER_DIM || is % 8) return KVPUB_ERR_INVALID_ARG;
+    if (ls < (int64_t)KVPUB_LATENT_DIM || ls % 8 || ls > INT32_MAX) return KVPUB_ERR_INVALID_ARG;
+    if (rs < (int64_t)KVPUB_ROPE_DIM || rs % 8 || rs > INT32_MAX) return KVPUB_ERR_INVALID_ARG;
+    if (is < (int64_t)KVPUB_INDEXER_DIM || is % 8 || is > INT32_MAX) return KVPUB_ERR_INVALID_ARG;
     return KVPUB_OK;
 }
 

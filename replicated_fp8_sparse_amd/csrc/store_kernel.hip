@@ -44,7 +44,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kE4m3Max = 448.0f;
-constexpr float kFastScaleMin = 0x1p-64f;
 constexpr int kNumXcds = 8;
 
 // Block b runs on XCD b % 8.  Give each XCD a contiguous range of token chunks
@@ -85,49 +84,44 @@ __device__ __forceinline__ uint32_t lane_amax_bits(u32x4 d) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// RN32(x / scale), clamped to the e4m3 range.  The clamp never changes the code
-// (anything in (448, 464) rounds to 448 anyway) but keeps the convert away
-// from its overflow behaviour.
-__device__ __forceinline__ float quotient_fast(float x, float scale, float inv) {
-    const float a = __builtin_fabsf(x);
-    const float q = a * inv;
-    const float r = __builtin_fmaf(-q, scale, a);
-    return __builtin_copysignf(__builtin_fminf(__builtin_fmaf(r, inv, q), kE4m3Max), x);
-}
-
-__device__ __forceinline__ float quotient_exact(float x, float scale) {
-    if (scale == 0.0f) return 0.0f;  // all-zero tile: codes 0x00, whatever the signs
-    const float q = x / scale;
-    return __builtin_copysignf(__builtin_fminf(__builtin_fabsf(q), kE4m3Max), q);
-}
-
-struct TileScale {
-    float scale;
-    float inv;
-    bool fast;
+// Exact tile scale and reciprocal from a 128-entry table.
+//
+// A tile's amax is a bf16 value (128 + m) * 2^(E-134), E its biased exponent
+// and m its 7 mantissa bits, so amax / 448 = ((128 + m) / 448) * 2^(E-134)
+// exactly.  Rounding to binary32 commutes with scaling by a power of two as
+// long as the result stays normal, hence
+//   RN(amax / 448)         = RN((128 + m) / 448) * 2^(E-134)
+//   RN(1 / RN(amax / 448)) = RN(1 / RN((128 + m) / 448)) * 2^(134-E).
+// Each wave fills its own table once (IEEE divisions, two entries per lane,
+// while its first loads are in flight) and applies the power of two with
+// ldexp.  Used only on the fast path (E >= 72: the scale is >= 2^-64 and
+// normal); other tiles divide.
+struct ScaleEntry {
+    float s;  // RN((128 + m) / 448)
+    float y;  // RN(1 / s)
 };
+__device__ __forceinline__ ScaleEntry scale_entry(uint32_t m) {
+    const float s = (float)(128u + m) / kE4m3Max;
+    return ScaleEntry{s, 1.0f / s};
+}
+constexpr uint32_t kFastMinExponent = 72;   // amax >= 2^-55  <=>  scale >= 2^-64
 
-__device__ __forceinline__ TileScale tile_scale(uint32_t amax_bits16) {
-    TileScale t;
-    t.scale = __uint_as_float(amax_bits16 << 16) / kE4m3Max;
-    t.fast = t.scale >= kFastScaleMin;
-    t.inv = t.fast ? 1.0f / t.scale : 0.0f;
-    return t;
+// RN32(x / scale) from the correctly rounded reciprocal y (see the header):
+// q = |x|*y, r = |x| - q*scale (exact, fused), q' = q + r*y, sign of x.
+__device__ __forceinline__ float quotient_fast(float x, float scale, float y) {
+    const float a = __builtin_fabsf(x);
+    const float q = a * y;
+    const float r = __builtin_fmaf(-q, scale, a);
+    return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
 }
 
-// Codes of the lane's 8 elements, in element order (byte e = element e).
-__device__ __forceinline__ u32x2 quant8(u32x4 d, const TileScale& t) {
-    float x[8] = {bf16_lo(d.x), bf16_hi(d.x), bf16_lo(d.y), bf16_hi(d.y),
-                  bf16_lo(d.z), bf16_hi(d.z), bf16_lo(d.w), bf16_hi(d.w)};
-    float q[8];
-    if (t.fast) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], t.scale, t.inv);
-    } else {
-        // all-zero tile (scale 0: codes 0x00) or a tiny scale: exact division
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = quotient_exact(x[e], t.scale);
-    }
+// IEEE division for tiles off the fast path; an all-zero tile gives +0
+// (codes 0x00 whatever the signs of its zeros).
+__device__ __forceinline__ float quotient_exact(float x, float scale) {
+    return scale == 0.0f ? 0.0f : x / scale;
+}
+
+__device__ __forceinline__ u32x2 cvt8(const float (&q)[8]) {
     int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
     int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
@@ -135,10 +129,11 @@ __device__ __forceinline__ u32x2 quant8(u32x4 d, const TileScale& t) {
     return u32x2{(uint32_t)w0, (uint32_t)w1};
 }
 
+__device__ __forceinline__ void unpack8(u32x4 d, float (&x)[8]) {
+    x[0] = bf16_lo(d.x); x[1] = bf16_hi(d.x); x[2] = bf16_lo(d.y); x[3] = bf16_hi(d.y);
+    x[4] = bf16_lo(d.z); x[5] = bf16_hi(d.z); x[6] = bf16_lo(d.w); x[7] = bf16_hi(d.w);
+}
 
-#ifndef KVPUB_XCD
-#define KVPUB_XCD 1
-#endif
 #ifndef KVPUB_WPC
 #define KVPUB_WPC 16   // target waves per CU before a block takes several block-groups
 #endif
@@ -157,26 +152,38 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// What the loads need; these arrive as separate kernel arguments so that the
+// hardware preloads them into SGPRs at wave launch (kernarg preloading), and
+// the loads can be issued without first waiting for a kernel-argument fetch.
+struct RowArgs {
+    const uint16_t* latent;
+    const uint16_t* rope;
+    const uint16_t* indexer;
+    const int64_t* slots;
+    int64_t num_tokens;
+    int32_t latent_stride, rope_stride, indexer_stride;   // elements
+};
+
 // Issue every load of a group.  Token indices past the end are clamped to the
 // last token (always in bounds) and their slots forced to -1.
-__device__ __forceinline__ void load_group(const StoreParams& p, int64_t t0, uint32_t lane, Group& G) {
-    const int64_t last = p.num_tokens - 1;
+__device__ __forceinline__ void load_group(const RowArgs& a, int64_t t0, uint32_t lane, Group& G) {
+    const int64_t last = a.num_tokens - 1;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int64_t t = t0 + k < last ? t0 + k : last;
-        G.lat[k] = ld16(p.latent + t * p.latent_stride + lane * 8);
+        G.lat[k] = ld16(a.latent + t * a.latent_stride + lane * 8);
     }
     const int64_t ug = t0 + (lane >> 4), ur = t0 + ((lane >> 3) & 3u);
     const int64_t tg = ug < last ? ug : last, tr = ur < last ? ur : last;
-    G.ix = ld16(p.indexer + tg * p.indexer_stride + (lane & 15u) * 8);
-    G.rp = ld16(p.rope + tr * p.rope_stride + (lane & 7u) * 8);
+    G.ix = ld16(a.indexer + tg * a.indexer_stride + (lane & 15u) * 8);
+    G.rp = ld16(a.rope + tr * a.rope_stride + (lane & 7u) * 8);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int64_t t = t0 + k < last ? t0 + k : last;
-        const int64_t v = p.slots[t];
+        const int64_t v = a.slots[t];
         G.s[k] = t0 + k <= last ? v : -1;
     }
-    const int64_t vg = p.slots[tg], vr = p.slots[tr];
+    const int64_t vg = a.slots[tg], vr = a.slots[tr];
     G.sg = ug <= last ? vg : -1;
     G.sr = ur <= last ? vr : -1;
 }
@@ -187,33 +194,73 @@ __device__ __forceinline__ bool slot_ok(int64_t s, int64_t capacity) {
 
 // Quantize a group and hand every output piece to `out`:
 //   out.codes(k, c)     Main-KV row bytes [8*lane, +8) of token k
-//   out.scales(k, v)    row bytes [512, 528) of token k (lane 0 only)
+//   out.scale(k, v)     row bytes [512 + 4*(lane/16), +4) of token k: the scale of
+//                       tile lane/16 (lanes 0, 16, 32, 48)
 //   out.rope(v)         row bytes [528 + 16*(lane%8), +16) of token lane/8 (lanes 0..31)
 //   out.icodes(c)       Indexer-K codes [8*(lane%16), +8) of token lane/16
 //   out.iscale(v)       Indexer-K scale of token lane/16 (lanes 16g only)
-// tok[k] (wave-uniform), ok_r and ok_g (per lane) select what is produced.
+// tok[k] (wave-uniform), ok_r and ok_g (per lane) select what is stored; tab is
+// the wave's copy of the scale table.  The five rounds are independent and are
+// computed as one straight-line block (their reductions, table reads and
+// divisions interleave); only the stores are conditional.
 template <class Out>
-__device__ __forceinline__ void quantize_group(const Group& G, uint32_t lane, const bool (&tok)[4],
-                                               bool ok_r, bool ok_g, Out& out) {
+__device__ __forceinline__ void quantize_group(const Group& G, uint32_t lane, const ScaleEntry* tab,
+                                               const bool (&tok)[4], bool ok_r, bool ok_g, Out& out) {
+    const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
+    uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
+#pragma unroll
+    for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(rows[i]));
+    ScaleEntry se[5];
+    bool fast = true;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        se[i] = tab[ab[i] & 127u];
+        const uint32_t E = ab[i] >> 7;
+        fast = fast && E >= kFastMinExponent && E < 255u;
+    }
+    u32x2 codes[5];
+    float scale[5];
+    if (__all(fast)) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int E = (int)(ab[i] >> 7);
+            const float s = __builtin_ldexpf(se[i].s, E - 134);
+            const float y = __builtin_ldexpf(se[i].y, 134 - E);
+            float x[8], q[8];
+            unpack8(rows[i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], s, y);
+            codes[i] = cvt8(q);
+            scale[i] = s;
+        }
+    } else {
+        // some tile of the wave has a tiny (possibly subnormal) scale or is all
+        // zeros: those tiles divide, the others take the fast path
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const uint32_t E = ab[i] >> 7;
+            const bool f = E >= kFastMinExponent && E < 255u;
+            const float s_fast = __builtin_ldexpf(se[i].s, (int)E - 134);
+            const float y = __builtin_ldexpf(se[i].y, 134 - (int)E);
+            const float s_exact = __uint_as_float(ab[i] << 16) / kE4m3Max;
+            float x[8], q[8];
+            unpack8(rows[i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[e], s_fast, y) : quotient_exact(x[e], s_exact);
+            codes[i] = cvt8(q);
+            scale[i] = f ? s_fast : s_exact;
+        }
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         if (!tok[k]) continue;
-        const TileScale ts = tile_scale(row_max16(lane_amax_bits(G.lat[k])));
-        out.codes(k, quant8(G.lat[k], ts));
-        const uint32_t sb = __float_as_uint(ts.scale);
-        const u32x4 scales = {(uint32_t)__builtin_amdgcn_readlane((int)sb, 0),
-                              (uint32_t)__builtin_amdgcn_readlane((int)sb, 16),
-                              (uint32_t)__builtin_amdgcn_readlane((int)sb, 32),
-                              (uint32_t)__builtin_amdgcn_readlane((int)sb, 48)};
-        if (lane == 0) out.scales(k, scales);
+        out.codes(k, codes[k]);
+        if ((lane & 15u) == 0) out.scale(k, __float_as_uint(scale[k]));
     }
     if (lane < 32 && ok_r) out.rope(G.rp);
-    // every row computes its indexer tile (the DPP reduction needs full rows)
-    const TileScale ts = tile_scale(row_max16(lane_amax_bits(G.ix)));
-    const u32x2 codes = quant8(G.ix, ts);
     if (ok_g) {
-        out.icodes(codes);
-        if ((lane & 15u) == 0) out.iscale(__float_as_uint(ts.scale));
+        out.icodes(codes[4]);
+        if ((lane & 15u) == 0) out.iscale(__float_as_uint(scale[4]));
     }
 }
 
@@ -227,14 +274,15 @@ struct ScatterOut {
         return (uint64_t)(s >> 6) * p.main_page_stride + (uint64_t)(s & 63) * 656u;
     }
     __device__ void codes(int k, u32x2 c) {
-        const uint64_t o = row_off(G.s[k]) + lane * 8u;
+        const uint64_t o = row_off(G.s[k]);  // wave-uniform
 #pragma unroll
-        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x2*>(p.main_base[r] + o) = c;
+        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x2*>((p.main_base[r] + o) + (uint32_t)(lane * 8u)) = c;
     }
-    __device__ void scales(int k, u32x4 v) {
-        const uint64_t o = row_off(G.s[k]) + 512u;
+    __device__ void scale(int k, uint32_t v) {
+        const uint64_t o = row_off(G.s[k]) + 512u;  // wave-uniform
 #pragma unroll
-        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(p.main_base[r] + o) = v;
+        for (int r = 0; r < R; ++r)
+            *reinterpret_cast<uint32_t*>((p.main_base[r] + o) + (uint32_t)((lane >> 4) * 4u)) = v;
     }
     __device__ void rope(u32x4 v) {
         const uint64_t o = row_off(G.sr) + 528u + (lane & 7u) * 16u;
@@ -257,32 +305,42 @@ struct ScatterOut {
 // Each wave owns a contiguous run of p.groups_per_wave groups (4 tokens each);
 // blocks are mapped XCD-aware so that neighbouring groups share an L2.
 template <int R>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(const StoreParams p) {
+__global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
+    const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer, const int64_t* slots,
+    int32_t num_tokens, uint32_t num_blocks, int32_t latent_stride, int32_t rope_stride,
+    int32_t indexer_stride, int32_t groups_per_wave, const StoreParams p) {
+    const RowArgs a{latent, rope, indexer, slots, num_tokens, latent_stride, rope_stride, indexer_stride};
+    __shared__ ScaleEntry tab_lds[kWavesPerBlock][128];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#if KVPUB_XCD
-    const uint32_t chunk = xcd_chunk(blockIdx.x, gridDim.x);
-#else
-    const uint32_t chunk = blockIdx.x;
-#endif
-    const int64_t ngroups = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave;
-    const int64_t g0 = ((int64_t)chunk * kWavesPerBlock + wave) * p.groups_per_wave;
-    const int64_t g1 = g0 + p.groups_per_wave < ngroups ? g0 + p.groups_per_wave : ngroups;
+    const uint32_t chunk = xcd_chunk(blockIdx.x, num_blocks);   // num_blocks == gridDim.x
+    const int64_t ngroups = ((int64_t)num_tokens + kTokensPerWave - 1) / kTokensPerWave;
+    const int64_t g0 = ((int64_t)chunk * kWavesPerBlock + wave) * groups_per_wave;
+    const int64_t g1 = g0 + groups_per_wave < ngroups ? g0 + groups_per_wave : ngroups;
+    ScaleEntry* tab = tab_lds[wave];  // the wave's own copy: no barrier needed
     for (int64_t g = g0; g < g1; ++g) {
         Group G;
-        load_group(p, g * kTokensPerWave, lane, G);
-        if (*p.status & kStatusPoisoned) return;  // a fence timed out: fail closed
+        load_group(a, g * kTokensPerWave, lane, G);
+        // Issued after the row loads, consumed only through the store masks below.
+        const bool poisoned = (*p.status & kStatusPoisoned) != 0;  // a fence timed out: fail closed
+        if (g == g0) {  // fill the wave's scale table while the loads are in flight
+            uint32_t m = lane;
+            asm volatile("" : "+v"(m));  // keeps the divisions below the row loads
+            tab[m] = scale_entry(m);
+            tab[64 + m] = scale_entry(64 + m);
+        }
         // Invalid (neither -1 nor a slot of the cache) slots are skipped and counted.
         uint32_t nbad = 0;
         bool tok[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            tok[k] = slot_ok(G.s[k], p.capacity);
-            nbad += (G.s[k] != -1 && !tok[k]) ? 1u : 0u;
+            tok[k] = !poisoned && slot_ok(G.s[k], p.capacity);
+            nbad += (G.s[k] != -1 && !slot_ok(G.s[k], p.capacity)) ? 1u : 0u;
         }
-        if (nbad != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
+        if (nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
         ScatterOut<R> out{p, G, lane};
-        quantize_group(G, lane, tok, slot_ok(G.sr, p.capacity), slot_ok(G.sg, p.capacity), out);
+        quantize_group(G, lane, tab, tok, !poisoned && slot_ok(G.sr, p.capacity),
+                       !poisoned && slot_ok(G.sg, p.capacity), out);
     }
 }
 
@@ -296,16 +354,18 @@ hipError_t launch_store(const StoreParams& p_in, uint32_t num_replicas, hipStrea
     const int64_t waves = (ngroups + p.groups_per_wave - 1) / p.groups_per_wave;
     const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 grid((uint32_t)blocks), block(kWavesPerBlock * 64);
+#define KVPUB_ROW_ARGS p.latent, p.rope, p.indexer, p.slots, (int32_t)p.num_tokens, (uint32_t)blocks, \
+    (int32_t)p.latent_stride, (int32_t)p.rope_stride, (int32_t)p.indexer_stride, (int32_t)p.groups_per_wave
     (void)hipGetLastError();
     switch (num_replicas) {
-        case 1: store_kernel<1><<<grid, block, 0, stream>>>(p); break;
-        case 2: store_kernel<2><<<grid, block, 0, stream>>>(p); break;
-        case 3: store_kernel<3><<<grid, block, 0, stream>>>(p); break;
-        case 4: store_kernel<4><<<grid, block, 0, stream>>>(p); break;
-        case 5: store_kernel<5><<<grid, block, 0, stream>>>(p); break;
-        case 6: store_kernel<6><<<grid, block, 0, stream>>>(p); break;
-        case 7: store_kernel<7><<<grid, block, 0, stream>>>(p); break;
-        case 8: store_kernel<8><<<grid, block, 0, stream>>>(p); break;
+        case 1: store_kernel<1><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
+        case 2: store_kernel<2><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
+        case 3: store_kernel<3><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
+        case 4: store_kernel<4><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
+        case 5: store_kernel<5><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
+        case 6: store_kernel<6><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
+        case 7: store_kernel<7><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
+        case 8: store_kernel<8><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
