@@ -21,7 +21,6 @@ struct kvpub_ctx {
     uint64_t* host_signals;    // P > 1: host-coherent signals [lanes][P] (kSignalStride apart)
     uint64_t* host_signals_dev;
     uint64_t timeout_ticks;
-    int32_t num_cus;
     hipStream_t capture_stream;
 };
 
@@ -151,7 +150,6 @@ StoreParams store_params(kvpub_ctx* ctx, uint32_t layer, int64_t T, const void* 
     }
     p.invalid_count = reinterpret_cast<unsigned long long*>(ctx->words + kvpub::kInvalidOffset);
     p.status = reinterpret_cast<const uint32_t*>(ctx->words + kvpub::kStatusOffset);
-    p.num_cus = ctx->num_cus;
     return p;
 }
 
@@ -220,7 +218,6 @@ KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_b
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, cfg->device) != hipSuccess) return KVPUB_ERR_HIP;
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KVPUB_ERR_UNSUPPORTED;
-    const int num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
 
     DeviceGuard guard(cfg->device);
     if (!guard.ok) return KVPUB_ERR_HIP;
@@ -229,7 +226,6 @@ KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_b
     if (!c) return KVPUB_ERR_OUT_OF_MEMORY;
     std::memset(c, 0, sizeof *c);
     c->cfg = *cfg;
-    c->num_cus = num_cus;
     for (uint32_t r = 0; r < cfg->num_replicas; ++r) {
         c->main_base[r] = static_cast<uint8_t*>(main_bases[r]);
         c->idx_base[r] = static_cast<uint8_t*>(idx_bases[r]);

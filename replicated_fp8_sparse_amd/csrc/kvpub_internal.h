@@ -13,6 +13,7 @@ constexpr int kTokensPerWave = 4;     // 4 tokens x 5 tiles = 5 rounds of 4 tile
 #endif
 constexpr int kWavesPerBlock = KVPUB_WPB;     // 256 threads, 16 tokens per block
 constexpr int kTokensPerBlock = kTokensPerWave * kWavesPerBlock;
+constexpr int64_t kMaxTokensPerLaunch = int64_t(1) << 24;   // larger batches take several launches
 
 constexpr uint32_t kStatusFenceTimeout = 0x1u;
 constexpr uint32_t kStatusPoisoned = 0x2u;
@@ -40,8 +41,6 @@ struct StoreParams {
     uint8_t* idx_base[kMaxReplicas];
     unsigned long long* invalid_count;
     const uint32_t* status;
-    int32_t num_cus;             // compute units of the device (sets the grid)
-    int64_t groups_per_wave;     // set by launch_store
 };
 
 struct FenceParams {

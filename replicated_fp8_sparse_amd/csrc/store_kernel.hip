@@ -41,7 +41,7 @@ namespace {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) uint8_t gbyte;   // a byte in global memory
 
 constexpr float kE4m3Max = 448.0f;
 constexpr int kNumXcds = 8;
@@ -69,22 +69,20 @@ __device__ __forceinline__ uint32_t row_max16(uint32_t v) {
     return v;
 }
 
-__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
-
-// Largest magnitude bit pattern among the lane's 8 bf16 values (sign cleared).
-// Non-negative finite floats order like their bit patterns.
-__device__ __forceinline__ uint32_t lane_amax_bits(u32x4 d) {
-    const uint32_t m = 0x7FFF7FFFu;
-    u16x2 a = __builtin_elementwise_max(as_u16x2(d.x & m), as_u16x2(d.y & m));
-    u16x2 b = __builtin_elementwise_max(as_u16x2(d.z & m), as_u16x2(d.w & m));
-    a = __builtin_elementwise_max(a, b);
-    return (uint32_t)(a.x > a.y ? a.x : a.y);
+// Binary32 bits of the largest magnitude among the lane's 8 values (finite
+// input: non-negative floats order like their bit patterns, and the maximum
+// is one of the bf16 inputs, so its low 16 bits are zero).
+__device__ __forceinline__ uint32_t lane_amax_bits(const float (&x)[8]) {
+    float m0 = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])), __builtin_fabsf(x[2]));
+    float m1 = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[3]), __builtin_fabsf(x[4])), __builtin_fabsf(x[5]));
+    float m2 = __builtin_fmaxf(__builtin_fmaxf(m0, m1), __builtin_fabsf(x[6]));
+    return __float_as_uint(__builtin_fmaxf(m2, __builtin_fabsf(x[7])));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Exact tile scale and reciprocal from a 128-entry table.
+// Exact tile scale and reciprocal without a division.
 //
 // A tile's amax is a bf16 value (128 + m) * 2^(E-134), E its biased exponent
 // and m its 7 mantissa bits, so amax / 448 = ((128 + m) / 448) * 2^(E-134)
@@ -92,27 +90,36 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // long as the result stays normal, hence
 //   RN(amax / 448)         = RN((128 + m) / 448) * 2^(E-134)
 //   RN(1 / RN(amax / 448)) = RN(1 / RN((128 + m) / 448)) * 2^(134-E).
-// Each wave fills its own table once (IEEE divisions, two entries per lane,
-// while its first loads are in flight) and applies the power of two with
-// ldexp.  Used only on the fast path (E >= 72: the scale is >= 2^-64 and
-// normal); other tiles divide.
-struct ScaleEntry {
-    float s;  // RN((128 + m) / 448)
+// For n = 128 + m, S = RN(n / 448) comes from q0 = n * RN(1/448) and one
+// remainder correction; Y = RN(1 / S) from the hardware reciprocal and one
+// Newton step with fused multiply-adds.  Both sequences reproduce the
+// correctly rounded values for all 128 mantissas (Y even when the reciprocal
+// estimate is off by up to 3 ulp); the check is part of the CPU tests.  Used
+// only on the fast path (E >= 72: the scale is >= 2^-64 and normal).
+struct TileScale {
+    float s;  // RN(amax / 448)
     float y;  // RN(1 / s)
 };
-__device__ __forceinline__ ScaleEntry scale_entry(uint32_t m) {
-    const float s = (float)(128u + m) / kE4m3Max;
-    return ScaleEntry{s, 1.0f / s};
+__device__ __forceinline__ TileScale tile_scale(uint32_t ab) {
+    const float n = (float)((ab & 127u) | 128u);
+    const float c = 1.0f / kE4m3Max;   // RN(1/448), folded at compile time
+    const float q0 = n * c;
+    const float S = __builtin_fmaf(__builtin_fmaf(-q0, kE4m3Max, n), c, q0);
+    const float y0 = __builtin_amdgcn_rcpf(S);
+    const float Y = __builtin_fmaf(__builtin_fmaf(-S, y0, 1.0f), y0, y0);
+    const int E = (int)(ab >> 7);
+    return TileScale{__builtin_ldexpf(S, E - 134), __builtin_ldexpf(Y, 134 - E)};
 }
 constexpr uint32_t kFastMinExponent = 72;   // amax >= 2^-55  <=>  scale >= 2^-64
 
 // RN32(x / scale) from the correctly rounded reciprocal y (see the header):
-// q = |x|*y, r = |x| - q*scale (exact, fused), q' = q + r*y, sign of x.
+// q = x*y, t = q*scale - x (exact, fused), q' = q - t*y.  Round-to-nearest
+// is symmetric, so this is the magnitude computation with the sign of x put
+// back, signed zeros included (x = -0 gives t = +0 and q' = -0).
 __device__ __forceinline__ float quotient_fast(float x, float scale, float y) {
-    const float a = __builtin_fabsf(x);
-    const float q = a * y;
-    const float r = __builtin_fmaf(-q, scale, a);
-    return __builtin_copysignf(__builtin_fmaf(r, y, q), x);
+    const float q = x * y;
+    const float t = __builtin_fmaf(q, scale, -x);
+    return __builtin_fmaf(-t, y, q);
 }
 
 // IEEE division for tiles off the fast path; an all-zero tile gives +0
@@ -134,87 +141,107 @@ __device__ __forceinline__ void unpack8(u32x4 d, float (&x)[8]) {
     x[4] = bf16_lo(d.z); x[5] = bf16_hi(d.z); x[6] = bf16_lo(d.w); x[7] = bf16_hi(d.w);
 }
 
-#ifndef KVPUB_WPC
-#define KVPUB_WPC 16   // target waves per CU before a block takes several block-groups
-#endif
-
-// One group = 4 consecutive tokens: their rows (loaded once) and slots.
+// The rows of one group = 4 consecutive tokens, loaded once.
 struct Group {
     u32x4 lat[4];    // latent of token k: lane l holds elements 8l..8l+7
     u32x4 ix;        // indexer of token g = l/16: elements 8(l%16)..+7
     u32x4 rp;        // RoPE of token (l/8)%4: elements 8(l%8)..+7 (lanes 32..63 repeat 0..31)
-    int64_t s[4];    // wave-uniform slots of the 4 tokens, -1 past the last token
-    int64_t sg;      // slot of this lane's indexer token
-    int64_t sr;      // slot of this lane's RoPE token
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// What the loads need; these arrive as separate kernel arguments so that the
-// hardware preloads them into SGPRs at wave launch (kernarg preloading), and
-// the loads can be issued without first waiting for a kernel-argument fetch.
-struct RowArgs {
-    const uint16_t* latent;
-    const uint16_t* rope;
-    const uint16_t* indexer;
-    const int64_t* slots;
-    int64_t num_tokens;
-    int32_t latent_stride, rope_stride, indexer_stride;   // elements
+// Where a group's pieces go, worked out from the slots while its rows are in
+// flight.  Offsets are bytes from a replica's layer base.
+template <int R>
+struct Dest {
+    gbyte* main[R];    // replica layer bases
+    gbyte* idx[R];
+    uint64_t row[4];   // Main-KV row of token k (wave-uniform)
+    uint32_t tok;      // bit k: token k is stored (wave-uniform)
+    uint64_t rope;     // this lane's RoPE piece (lanes 0..31)
+    uint64_t icode;    // this lane's Indexer-K code piece
+    uint64_t iscale;   // this lane's Indexer-K scale (all 16 lanes of a row)
+    uint32_t ok_r, ok_g;   // this lane's RoPE / Indexer-K token is stored
 };
-
-// Issue every load of a group.  Token indices past the end are clamped to the
-// last token (always in bounds) and their slots forced to -1.
-__device__ __forceinline__ void load_group(const RowArgs& a, int64_t t0, uint32_t lane, Group& G) {
-    const int64_t last = a.num_tokens - 1;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t t = t0 + k < last ? t0 + k : last;
-        G.lat[k] = ld16(a.latent + t * a.latent_stride + lane * 8);
-    }
-    const int64_t ug = t0 + (lane >> 4), ur = t0 + ((lane >> 3) & 3u);
-    const int64_t tg = ug < last ? ug : last, tr = ur < last ? ur : last;
-    G.ix = ld16(a.indexer + tg * a.indexer_stride + (lane & 15u) * 8);
-    G.rp = ld16(a.rope + tr * a.rope_stride + (lane & 7u) * 8);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t t = t0 + k < last ? t0 + k : last;
-        const int64_t v = a.slots[t];
-        G.s[k] = t0 + k <= last ? v : -1;
-    }
-    const int64_t vg = a.slots[tg], vr = a.slots[tr];
-    G.sg = ug <= last ? vg : -1;
-    G.sr = ur <= last ? vr : -1;
-}
 
 __device__ __forceinline__ bool slot_ok(int64_t s, int64_t capacity) {
     return (uint64_t)s < (uint64_t)capacity;   // negative slots wrap to huge values
 }
 
-// Quantize a group and hand every output piece to `out`:
-//   out.codes(k, c)     Main-KV row bytes [8*lane, +8) of token k
-//   out.scale(k, v)     row bytes [512 + 4*(lane/16), +4) of token k: the scale of
-//                       tile lane/16 (lanes 0, 16, 32, 48)
-//   out.rope(v)         row bytes [528 + 16*(lane%8), +16) of token lane/8 (lanes 0..31)
-//   out.icodes(c)       Indexer-K codes [8*(lane%16), +8) of token lane/16
-//   out.iscale(v)       Indexer-K scale of token lane/16 (lanes 16g only)
-// tok[k] (wave-uniform), ok_r and ok_g (per lane) select what is stored; tab is
-// the wave's copy of the scale table.  The five rounds are independent and are
-// computed as one straight-line block (their reductions, table reads and
-// divisions interleave); only the stores are conditional.
-template <class Out>
-__device__ __forceinline__ void quantize_group(const Group& G, uint32_t lane, const ScaleEntry* tab,
-                                               const bool (&tok)[4], bool ok_r, bool ok_g, Out& out) {
+// v_i for a per-lane index i in 0..3; v0..v3 wave-uniform.
+__device__ __forceinline__ uint64_t pick4(uint64_t v0, uint64_t v1, uint64_t v2, uint64_t v3, uint32_t i) {
+    const uint64_t a = (i & 1u) ? v1 : v0;
+    const uint64_t b = (i & 1u) ? v3 : v2;
+    return (i & 2u) ? b : a;
+}
+
+// The value is materialized in a register at this point, so later code
+// cannot pull its computation below (past the wait for the row data).
+__device__ __forceinline__ uint64_t pin_s(uint64_t v) { asm volatile("" : "+s"(v)); return v; }
+__device__ __forceinline__ uint64_t pin_v(uint64_t v) { asm volatile("" : "+v"(v)); return v; }
+__device__ __forceinline__ uint32_t pin_v32(uint32_t v) { asm volatile("" : "+v"(v)); return v; }
+__device__ __forceinline__ gbyte* pin_ptr(uint8_t* v) {
+    gbyte* g = (gbyte*)v;
+    asm volatile("" : "+s"(g));
+    return g;
+}
+
+template <int R>
+__device__ __forceinline__ Dest<R> destinations(int64_t s0, int64_t s1, int64_t s2, int64_t s3, bool poisoned,
+                                             uint32_t lane, const StoreParams& p) {
+    const int64_t sl[4] = {s0, s1, s2, s3};
+    uint64_t row[4], irow[4], iscl[4];
+    uint32_t tok = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint64_t page = (uint64_t)sl[k] >> 6, in = (uint64_t)sl[k] & 63u;
+        row[k] = pin_s(page * p.main_page_stride + in * 656u);
+        irow[k] = page * p.idx_page_stride + in * 128u;
+        iscl[k] = page * p.idx_page_stride + 8192u + in * 4u;
+        tok |= (!poisoned && slot_ok(sl[k], p.capacity)) ? (1u << k) : 0u;
+    }
+    const uint32_t g = lane >> 4, r = (lane >> 3) & 3u;
+    Dest<R> d;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        d.main[i] = pin_ptr(p.main_base[i]);
+        d.idx[i] = pin_ptr(p.idx_base[i]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) d.row[k] = row[k];
+    tok = __builtin_amdgcn_readfirstlane(tok);   // uniform; computed once, before the wait
+    asm volatile("" : "+s"(tok));
+    d.tok = tok;
+    d.rope = pin_v(pick4(row[0], row[1], row[2], row[3], r) + 528u + (lane & 7u) * 16u);
+    d.icode = pin_v(pick4(irow[0], irow[1], irow[2], irow[3], g) + (lane & 15u) * 8u);
+    d.iscale = pin_v(pick4(iscl[0], iscl[1], iscl[2], iscl[3], g));
+    d.ok_r = pin_v32(lane < 32u ? (tok >> r) & 1u : 0u);
+    d.ok_g = pin_v32((tok >> g) & 1u);
+    return d;
+}
+
+// Quantize a group and store every piece to each of the R replicas:
+//   codes of token k  -> row bytes [8*lane, +8)
+//   scale of tile j   -> row bytes [512 + 4j, +4)       (lane 16j)
+//   RoPE              -> row bytes [528 + 16*(lane%8), +16) of token lane/8 (lanes 0..31)
+//   Indexer-K codes   -> page bytes [128*(slot%64) + 8*(lane%16), +8) of token lane/16
+//   Indexer-K scale   -> page bytes [8192 + 4*(slot%64), +4) (lane 16g)
+// The five rounds are computed as one straight-line block (their reductions
+// and scale sequences interleave); only the stores are conditional.
+template <int R>
+__device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d, uint32_t lane) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
+    float x[5][8];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) unpack8(rows[i], x[i]);
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
 #pragma unroll
-    for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(rows[i]));
-    ScaleEntry se[5];
+    for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(x[i])) >> 16;
     bool fast = true;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-        se[i] = tab[ab[i] & 127u];
         const uint32_t E = ab[i] >> 7;
         fast = fast && E >= kFastMinExponent && E < 255u;
     }
@@ -223,15 +250,12 @@ __device__ __forceinline__ void quantize_group(const Group& G, uint32_t lane, co
     if (__all(fast)) {
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
-            const int E = (int)(ab[i] >> 7);
-            const float s = __builtin_ldexpf(se[i].s, E - 134);
-            const float y = __builtin_ldexpf(se[i].y, 134 - E);
-            float x[8], q[8];
-            unpack8(rows[i], x);
+            const TileScale t = tile_scale(ab[i]);
+            float q[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], s, y);
+            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[i][e], t.s, t.y);
             codes[i] = cvt8(q);
-            scale[i] = s;
+            scale[i] = t.s;
         }
     } else {
         // some tile of the wave has a tiny (possibly subnormal) scale or is all
@@ -240,135 +264,125 @@ __device__ __forceinline__ void quantize_group(const Group& G, uint32_t lane, co
         for (int i = 0; i < 5; ++i) {
             const uint32_t E = ab[i] >> 7;
             const bool f = E >= kFastMinExponent && E < 255u;
-            const float s_fast = __builtin_ldexpf(se[i].s, (int)E - 134);
-            const float y = __builtin_ldexpf(se[i].y, 134 - (int)E);
+            const TileScale t = tile_scale(ab[i]);
             const float s_exact = __uint_as_float(ab[i] << 16) / kE4m3Max;
-            float x[8], q[8];
-            unpack8(rows[i], x);
+            float q[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[e], s_fast, y) : quotient_exact(x[e], s_exact);
+            for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[i][e], t.s, t.y) : quotient_exact(x[i][e], s_exact);
             codes[i] = cvt8(q);
-            scale[i] = f ? s_fast : s_exact;
+            scale[i] = f ? t.s : s_exact;
         }
     }
+    // A tile's scale is the same in all 16 lanes of its row; the 16 lanes
+    // store it to the same word, which the memory pipeline merges.
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        if (!tok[k]) continue;
-        out.codes(k, codes[k]);
-        if ((lane & 15u) == 0) out.scale(k, __float_as_uint(scale[k]));
+        if (!((d.tok >> k) & 1u)) continue;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            gbyte* row = d.main[r] + d.row[k];
+            *reinterpret_cast<__attribute__((address_space(1))) u32x2*>(row + lane * 8u) = codes[k];
+            *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(row + 512u + (lane >> 4) * 4u) =
+                __float_as_uint(scale[k]);
+        }
     }
-    if (lane < 32 && ok_r) out.rope(G.rp);
-    if (ok_g) {
-        out.icodes(codes[4]);
-        if ((lane & 15u) == 0) out.iscale(__float_as_uint(scale[4]));
+    if (d.ok_r) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(d.main[r] + d.rope) = G.rp;
+    }
+    if (d.ok_g) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            *reinterpret_cast<__attribute__((address_space(1))) u32x2*>(d.idx[r] + d.icode) = codes[4];
+            *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(d.idx[r] + d.iscale) =
+                __float_as_uint(scale[4]);
+        }
     }
 }
 
-// Stores each piece at its slot in every replica.
-template <int R>
-struct ScatterOut {
-    const StoreParams& p;
-    const Group& G;
-    uint32_t lane;
-    __device__ uint64_t row_off(int64_t s) const {
-        return (uint64_t)(s >> 6) * p.main_page_stride + (uint64_t)(s & 63) * 656u;
-    }
-    __device__ void codes(int k, u32x2 c) {
-        const uint64_t o = row_off(G.s[k]);  // wave-uniform
-#pragma unroll
-        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x2*>((p.main_base[r] + o) + (uint32_t)(lane * 8u)) = c;
-    }
-    __device__ void scale(int k, uint32_t v) {
-        const uint64_t o = row_off(G.s[k]) + 512u;  // wave-uniform
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            *reinterpret_cast<uint32_t*>((p.main_base[r] + o) + (uint32_t)((lane >> 4) * 4u)) = v;
-    }
-    __device__ void rope(u32x4 v) {
-        const uint64_t o = row_off(G.sr) + 528u + (lane & 7u) * 16u;
-#pragma unroll
-        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x4*>(p.main_base[r] + o) = v;
-    }
-    __device__ void icodes(u32x2 c) {
-        const uint64_t o = (uint64_t)(G.sg >> 6) * p.idx_page_stride + (uint64_t)(G.sg & 63) * 128u +
-                           (lane & 15u) * 8u;
-#pragma unroll
-        for (int r = 0; r < R; ++r) *reinterpret_cast<u32x2*>(p.idx_base[r] + o) = c;
-    }
-    __device__ void iscale(uint32_t v) {
-        const uint64_t o = (uint64_t)(G.sg >> 6) * p.idx_page_stride + 8192u + (uint64_t)(G.sg & 63) * 4u;
-#pragma unroll
-        for (int r = 0; r < R; ++r) *reinterpret_cast<uint32_t*>(p.idx_base[r] + o) = v;
-    }
-};
-
-// Each wave owns a contiguous run of p.groups_per_wave groups (4 tokens each);
-// blocks are mapped XCD-aware so that neighbouring groups share an L2.
+// One group per wave; blocks are mapped XCD-aware so that neighbouring
+// groups share an L2.  The arguments before p are what the first
+// instructions need: they arrive preloaded in SGPRs (kernel-argument
+// preloading); p is fetched while the row loads are in flight.  Token
+// indices are 32-bit (a launch holds at most kMaxTokensPerLaunch tokens).
 template <int R>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
-    const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer, const int64_t* slots,
-    int32_t num_tokens, uint32_t num_blocks, int32_t latent_stride, int32_t rope_stride,
-    int32_t indexer_stride, int32_t groups_per_wave, const StoreParams p) {
-    const RowArgs a{latent, rope, indexer, slots, num_tokens, latent_stride, rope_stride, indexer_stride};
-    __shared__ ScaleEntry tab_lds[kWavesPerBlock][128];
+    const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
+    const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
+    uint32_t indexer_stride, const uint32_t* __restrict__ status, const StoreParams p) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t chunk = xcd_chunk(blockIdx.x, num_blocks);   // num_blocks == gridDim.x
-    const int64_t ngroups = ((int64_t)num_tokens + kTokensPerWave - 1) / kTokensPerWave;
-    const int64_t g0 = ((int64_t)chunk * kWavesPerBlock + wave) * groups_per_wave;
-    const int64_t g1 = g0 + groups_per_wave < ngroups ? g0 + groups_per_wave : ngroups;
-    ScaleEntry* tab = tab_lds[wave];  // the wave's own copy: no barrier needed
-    for (int64_t g = g0; g < g1; ++g) {
-        Group G;
-        load_group(a, g * kTokensPerWave, lane, G);
-        // Issued after the row loads, consumed only through the store masks below.
-        const bool poisoned = (*p.status & kStatusPoisoned) != 0;  // a fence timed out: fail closed
-        if (g == g0) {  // fill the wave's scale table while the loads are in flight
-            uint32_t m = lane;
-            asm volatile("" : "+v"(m));  // keeps the divisions below the row loads
-            tab[m] = scale_entry(m);
-            tab[64 + m] = scale_entry(64 + m);
-        }
-        // Invalid (neither -1 nor a slot of the cache) slots are skipped and counted.
-        uint32_t nbad = 0;
-        bool tok[4];
+    const uint32_t num_blocks = (num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;   // == gridDim.x
+    const uint32_t t0 = (xcd_chunk(blockIdx.x, num_blocks) * kWavesPerBlock + wave) * kTokensPerWave;
+    if (t0 >= num_tokens) return;
+    const uint32_t last = num_tokens - 1;
+    // Scalar loads (slots of the 4 tokens, the status word) do not share a
+    // counter with the row loads, so the destinations are worked out before
+    // the rows arrive.  Token indices past the end are clamped to the last
+    // token (always in bounds); their slots become -1.
+    int64_t sl[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            tok[k] = !poisoned && slot_ok(G.s[k], p.capacity);
-            nbad += (G.s[k] != -1 && !slot_ok(G.s[k], p.capacity)) ? 1u : 0u;
-        }
-        if (nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
-        ScatterOut<R> out{p, G, lane};
-        quantize_group(G, lane, tab, tok, !poisoned && slot_ok(G.sr, p.capacity),
-                       !poisoned && slot_ok(G.sg, p.capacity), out);
+    for (int k = 0; k < 4; ++k) sl[k] = slots[t0 + k < last ? t0 + k : last];
+    const uint32_t st = *status;
+    // Row loads in order of first use: the RoPE piece (stored unchanged)
+    // first, so that no wait for it lands among the stores, where it would
+    // also wait for every store issued before it.
+    Group G;
+    const uint32_t ug = t0 + (lane >> 4), ur = t0 + ((lane >> 3) & 3u);
+    const uint32_t tg = ug < last ? ug : last, tr = ur < last ? ur : last;
+    G.rp = ld16(rope + (uint64_t)tr * rope_stride + (lane & 7u) * 8u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t t = t0 + k < last ? t0 + k : last;
+        G.lat[k] = ld16(latent + (uint64_t)t * latent_stride + lane * 8u);
     }
+    G.ix = ld16(indexer + (uint64_t)tg * indexer_stride + (lane & 15u) * 8u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sl[k] = t0 + k <= last ? sl[k] : -1;
+    const bool poisoned = (st & kStatusPoisoned) != 0;  // a fence timed out: fail closed
+    // Invalid (neither -1 nor a slot of the cache) slots are skipped and counted.
+    uint32_t nbad = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) nbad += (sl[k] != -1 && !slot_ok(sl[k], p.capacity)) ? 1u : 0u;
+    if (nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
+    const Dest<R> d = destinations<R>(sl[0], sl[1], sl[2], sl[3], poisoned, lane, p);
+    __builtin_amdgcn_sched_barrier(0);
+    quantize_store<R>(G, d, lane);
 }
 
 }  // namespace
 
-hipError_t launch_store(const StoreParams& p_in, uint32_t num_replicas, hipStream_t stream) {
-    StoreParams p = p_in;
-    const int64_t ngroups = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave;
-    const int64_t max_waves = (int64_t)p.num_cus * KVPUB_WPC;
-    p.groups_per_wave = ngroups <= max_waves ? 1 : (ngroups + max_waves - 1) / max_waves;
-    const int64_t waves = (ngroups + p.groups_per_wave - 1) / p.groups_per_wave;
-    const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    const dim3 grid((uint32_t)blocks), block(kWavesPerBlock * 64);
-#define KVPUB_ROW_ARGS p.latent, p.rope, p.indexer, p.slots, (int32_t)p.num_tokens, (uint32_t)blocks, \
-    (int32_t)p.latent_stride, (int32_t)p.rope_stride, (int32_t)p.indexer_stride, (int32_t)p.groups_per_wave
+hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream) {
+    if (num_replicas < 1 || num_replicas > (uint32_t)kMaxReplicas) return hipErrorInvalidValue;
+    // One wave per group of 4 tokens; batches beyond kMaxTokensPerLaunch are
+    // split so that the grid stays far inside its limits.
     (void)hipGetLastError();
-    switch (num_replicas) {
-        case 1: store_kernel<1><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        case 2: store_kernel<2><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        case 3: store_kernel<3><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        case 4: store_kernel<4><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        case 5: store_kernel<5><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        case 6: store_kernel<6><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        case 7: store_kernel<7><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        case 8: store_kernel<8><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS, p); break;
-        default: return hipErrorInvalidValue;
+    for (int64_t t = 0; t < p.num_tokens; t += kMaxTokensPerLaunch) {
+        const int64_t n = p.num_tokens - t < kMaxTokensPerLaunch ? p.num_tokens - t : kMaxTokensPerLaunch;
+        const uint32_t blocks = (uint32_t)((n + kTokensPerBlock - 1) / kTokensPerBlock);
+        const dim3 grid(blocks), block(kWavesPerBlock * 64);
+        const uint16_t* lat = p.latent + t * p.latent_stride;
+        const uint16_t* rp = p.rope + t * p.rope_stride;
+        const uint16_t* ix = p.indexer + t * p.indexer_stride;
+        const int64_t* sl = p.slots + t;
+#define KVPUB_ROW_ARGS lat, rp, ix, sl, (uint32_t)n, (uint32_t)p.latent_stride, (uint32_t)p.rope_stride, \
+    (uint32_t)p.indexer_stride, p.status, p
+        switch (num_replicas) {
+            case 1: store_kernel<1><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+            case 2: store_kernel<2><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+            case 3: store_kernel<3><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+            case 4: store_kernel<4><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+            case 5: store_kernel<5><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+            case 6: store_kernel<6><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+            case 7: store_kernel<7><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+            default: store_kernel<8><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        }
+#undef KVPUB_ROW_ARGS
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace kvpub
