@@ -10,13 +10,16 @@
 // overlapped micro-batches.
 //
 // Protocol per lane, run by lane 0 of one wavefront:
-//   e = epoch[lane] + 1, written back with a system-scope release RMW;
-//   signal[self] = e (system-scope release store);
-//   for every participant q: acquire-load signal[q] until it is >= e.
-// The expected value e is read from device memory, never passed as a kernel
-// argument, so replaying a captured launch keeps advancing the epoch.  On one
-// GPU there is one participant (this GPU) and the wait ends at once; with
-// host-driven peers the other signals live in host-coherent memory.
+//   e = epoch[lane] + 1, by an acquire-release RMW at system scope: every
+//       write this GPU made before the fence is visible before the epoch
+//       moves, and what was published before it is visible after;
+//   signal[self] = e (a release store when there are peers to see it);
+//   for every other participant q: acquire-load signal[q] until it is >= e.
+// This GPU's own signal is never awaited: it was written just before, in
+// program order, by the same wave.  The expected value e is read from device
+// memory, never passed as a kernel argument, so replaying a captured launch
+// keeps advancing the epoch.  With host-driven peers the other signals live
+// in host-coherent memory.
 // The wait is bounded by the wall clock (s_memrealtime).  On timeout the
 // kernel sets the timeout and poisoned flags and returns normally; stores and
 // fences of a poisoned context write nothing.
@@ -25,21 +28,29 @@
 namespace kvpub {
 namespace {
 
-__global__ __launch_bounds__(64) void fence_kernel(const FenceParams p) {
+// Plain scalar arguments, so that they arrive preloaded in SGPRs.
+__global__ __launch_bounds__(64) void fence_kernel(uint64_t* epoch, uint64_t* signals, uint32_t* status,
+                                                   uint32_t num_participants, uint32_t self,
+                                                   uint64_t timeout_ticks) {
     if (threadIdx.x != 0) return;
-    if (__hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusPoisoned)
-        return;
+    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusPoisoned) return;
     const uint64_t e =
-        __hip_atomic_fetch_add(p.epoch, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM) + 1;
-    __hip_atomic_store(p.signals + (size_t)p.self * kSignalStride, e, __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM) + 1;
+    uint64_t* own = signals + (size_t)self * kSignalStride;
+    if (num_participants == 1) {
+        // no peer reads it: the RMW above already released and acquired
+        __hip_atomic_store(own, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        return;
+    }
+    __hip_atomic_store(own, e, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     const uint64_t start = wall_clock64();
-    for (uint32_t q = 0; q < p.num_participants; ++q) {
-        const uint64_t* sig = p.signals + (size_t)q * kSignalStride;
+    for (uint32_t q = 0; q < num_participants; ++q) {
+        if (q == self) continue;
+        const uint64_t* sig = signals + (size_t)q * kSignalStride;
         while (__hip_atomic_load(sig, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < e) {
-            if (wall_clock64() - start > p.timeout_ticks) {
-                __hip_atomic_fetch_or(p.status, kStatusFenceTimeout | kStatusPoisoned,
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (wall_clock64() - start > timeout_ticks) {
+                __hip_atomic_fetch_or(status, kStatusFenceTimeout | kStatusPoisoned, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
                 return;
             }
             __builtin_amdgcn_s_sleep(2);
@@ -51,7 +62,8 @@ __global__ __launch_bounds__(64) void fence_kernel(const FenceParams p) {
 
 hipError_t launch_fence(const FenceParams& p, hipStream_t stream) {
     (void)hipGetLastError();
-    fence_kernel<<<dim3(1), dim3(64), 0, stream>>>(p);
+    fence_kernel<<<dim3(1), dim3(64), 0, stream>>>(p.epoch, p.signals, p.status, p.num_participants, p.self,
+                                                   p.timeout_ticks);
     return hipGetLastError();
 }
 

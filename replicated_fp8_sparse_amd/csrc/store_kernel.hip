@@ -17,19 +17,21 @@
 // Lanes 0..31 also carry the 4 tokens' RoPE rows (8 lanes x 16 B each), which
 // are copied through unchanged.  Every input byte is loaded once, up front,
 // with token indices clamped to the last token so no load waits on a branch
-// or on the slot values.
+// or on the slot values; the slots arrive through scalar loads and every
+// store address is worked out while the rows are in flight.
 //
-// Per tile: amax from the bf16 magnitude bits (packed u16 max in-lane, then a
-// 4-step DPP max within the row), scale = amax / 448 (IEEE binary32
-// division), and per element code = e4m3fn(RN32(x / scale)).  RN32(x/scale)
-// is computed as q = |x|*y, r = fma(-q, scale, |x|), q' = fma(r, y, q) with
-// y = RN32(1/scale), sign restored from x.  For every scale >= 2^-64 this
-// gives the same e4m3 code as a correctly rounded division for every bf16 x
-// with |x| <= amax (the domain is finite and was checked exhaustively on the
-// CPU); tiles with a smaller scale (and all-zero tiles) take the plain IEEE
-// division path.  The conversion uses the gfx950 OCP e4m3 convert
-// (round-to-nearest-even); |x/scale| < 450 for finite input, below the
-// saturation boundary at 464, and quotients are clamped to 448 first.
+// Per tile: amax = the largest magnitude (max3 in-lane, then a 4-step DPP
+// max within the row), scale = RN32(amax / 448), and per element code =
+// e4m3fn(RN32(x / scale)).  The scale and its reciprocal y = RN32(1/scale)
+// come from a short exact sequence (tile_scale); RN32(x/scale) is computed as
+// q = x*y, t = fma(q, scale, -x), q' = fma(-t, y, q), which is the magnitude
+// form fma(fma(-|x|y, scale, |x|), y, |x|y) with the sign of x put back.
+// For every scale >= 2^-64 this gives the same e4m3 code as a correctly
+// rounded division for every bf16 x with |x| <= amax (the domain is finite
+// and was checked exhaustively on the CPU); tiles with a smaller scale (and
+// all-zero tiles) take the plain IEEE division path.  The conversion uses the
+// gfx950 OCP e4m3 convert (round-to-nearest-even, saturating only above 464):
+// |x/scale| <= 448 (1 + 2^-23) for finite input, so no clamp is needed.
 //
 // Every piece is stored straight to its slot in each replica (ordinary
 // write-back stores, so neighbouring pieces of a 128-byte line merge in L2);
