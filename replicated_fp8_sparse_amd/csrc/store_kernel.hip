@@ -43,7 +43,19 @@ namespace {
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) uint8_t gbyte;   // a byte in global memory
+typedef __attribute__((address_space(3))) uint8_t lbyte;   // a byte in LDS
+template <class T> using gptr = __attribute__((address_space(1))) T*;
+template <class T> using lptr = __attribute__((address_space(3))) T*;
+
+#ifndef KVPUB_MIN_WAVES
+#define KVPUB_MIN_WAVES 1   // minimum resident waves per SIMD the register budget must allow
+#endif
+#ifndef KVPUB_ROW_RUN
+#define KVPUB_ROW_RUN 1   // assemble runs of 4 consecutive rows in LDS and store them whole
+#endif
+constexpr uint32_t kRunBytes = 4 * 656;   // 2624 = 164 x 16 B
 
 constexpr float kE4m3Max = 448.0f;
 constexpr int kNumXcds = 8;
@@ -71,14 +83,18 @@ __device__ __forceinline__ uint32_t row_max16(uint32_t v) {
     return v;
 }
 
-// Binary32 bits of the largest magnitude among the lane's 8 values (finite
-// input: non-negative floats order like their bit patterns, and the maximum
-// is one of the bf16 inputs, so its low 16 bits are zero).
-__device__ __forceinline__ uint32_t lane_amax_bits(const float (&x)[8]) {
-    float m0 = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])), __builtin_fabsf(x[2]));
-    float m1 = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[3]), __builtin_fabsf(x[4])), __builtin_fabsf(x[5]));
-    float m2 = __builtin_fmaxf(__builtin_fmaxf(m0, m1), __builtin_fabsf(x[6]));
-    return __float_as_uint(__builtin_fmaxf(m2, __builtin_fabsf(x[7])));
+// bf16 magnitude bits of the largest magnitude among the lane's 8 values,
+// from the packed data (sign cleared: non-negative finite values order like
+// their bit patterns; two 16-bit maxima per instruction).  Working on the
+// packed rows keeps the unpacked values out of the registers until each
+// round's quotients need them.
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t lane_amax_bits(u32x4 d) {
+    const uint32_t m = 0x7FFF7FFFu;
+    u16x2 a = __builtin_elementwise_max(as_u16x2(d.x & m), as_u16x2(d.y & m));
+    u16x2 b = __builtin_elementwise_max(as_u16x2(d.z & m), as_u16x2(d.w & m));
+    a = __builtin_elementwise_max(a, b);
+    return (uint32_t)(a.x > a.y ? a.x : a.y);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -166,6 +182,7 @@ struct Dest {
     uint64_t icode;    // this lane's Indexer-K code piece
     uint64_t iscale;   // this lane's Indexer-K scale (all 16 lanes of a row)
     uint32_t ok_r, ok_g;   // this lane's RoPE / Indexer-K token is stored
+    uint32_t run;      // the 4 rows are consecutive slots of one page (wave-uniform)
 };
 
 __device__ __forceinline__ bool slot_ok(int64_t s, int64_t capacity) {
@@ -215,7 +232,12 @@ __device__ __forceinline__ Dest<R> destinations(int64_t s0, int64_t s1, int64_t 
     for (int k = 0; k < 4; ++k) d.row[k] = row[k];
     tok = __builtin_amdgcn_readfirstlane(tok);   // uniform; computed once, before the wait
     asm volatile("" : "+s"(tok));
+    uint32_t run = (KVPUB_ROW_RUN && tok == 0xFu && s1 == s0 + 1 && s2 == s0 + 2 && s3 == s0 + 3 && (s0 & 63) <= 60)
+                       ? 1u : 0u;
+    run = __builtin_amdgcn_readfirstlane(run);
+    asm volatile("" : "+s"(run));
     d.tok = tok;
+    d.run = run;
     d.rope = pin_v(pick4(row[0], row[1], row[2], row[3], r) + 528u + (lane & 7u) * 16u);
     d.icode = pin_v(pick4(irow[0], irow[1], irow[2], irow[3], g) + (lane & 15u) * 8u);
     d.iscale = pin_v(pick4(iscl[0], iscl[1], iscl[2], iscl[3], g));
@@ -233,14 +255,11 @@ __device__ __forceinline__ Dest<R> destinations(int64_t s0, int64_t s1, int64_t 
 // The five rounds are computed as one straight-line block (their reductions
 // and scale sequences interleave); only the stores are conditional.
 template <int R>
-__device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d, uint32_t lane) {
+__device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d, uint32_t lane, lbyte* img) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
-    float x[5][8];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) unpack8(rows[i], x[i]);
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
 #pragma unroll
-    for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(x[i])) >> 16;
+    for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(rows[i]));
     bool fast = true;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
@@ -253,9 +272,10 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d,
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             const TileScale t = tile_scale(ab[i]);
-            float q[8];
+            float x[8], q[8];
+            unpack8(rows[i], x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[i][e], t.s, t.y);
+            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], t.s, t.y);
             codes[i] = cvt8(q);
             scale[i] = t.s;
         }
@@ -268,36 +288,62 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d,
             const bool f = E >= kFastMinExponent && E < 255u;
             const TileScale t = tile_scale(ab[i]);
             const float s_exact = __uint_as_float(ab[i] << 16) / kE4m3Max;
-            float q[8];
+            float x[8], q[8];
+            unpack8(rows[i], x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[i][e], t.s, t.y) : quotient_exact(x[i][e], s_exact);
+            for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[e], t.s, t.y) : quotient_exact(x[e], s_exact);
             codes[i] = cvt8(q);
             scale[i] = f ? t.s : s_exact;
         }
     }
-    // A tile's scale is the same in all 16 lanes of its row; the 16 lanes
-    // store it to the same word, which the memory pipeline merges.
+    if (d.run) {
+        // The four rows are one contiguous 2624-byte run (656 = 41 x 16): build
+        // it in the wave's LDS image and store it as 16-byte pieces, three
+        // wave-wide stores per replica instead of nine partial-line ones.
+        // Only this wave touches its image, and LDS accesses of one wave
+        // complete in order, so no barrier is needed.
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if (!((d.tok >> k) & 1u)) continue;
+        for (int k = 0; k < 4; ++k) *(lptr<u32x2>)(img + k * 656u + lane * 8u) = codes[k];
+        if ((lane & 15u) == 0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                *(lptr<uint32_t>)(img + k * 656u + 512u + (lane >> 4) * 4u) = __float_as_uint(scale[k]);
+        }
+        if (lane < 32u) *(lptr<u32x4>)(img + ((lane >> 3) & 3u) * 656u + 528u + (lane & 7u) * 16u) = G.rp;
+        __builtin_amdgcn_wave_barrier();
+        const u32x4 c0 = *(lptr<u32x4>)(img + lane * 16u);
+        const u32x4 c1 = *(lptr<u32x4>)(img + 1024u + lane * 16u);
+        const u32x4 c2 = lane < 36u ? *(lptr<u32x4>)(img + 2048u + lane * 16u) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            gbyte* row = d.main[r] + d.row[k];
-            *reinterpret_cast<__attribute__((address_space(1))) u32x2*>(row + lane * 8u) = codes[k];
-            *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(row + 512u + (lane >> 4) * 4u) =
-                __float_as_uint(scale[k]);
+            gbyte* run0 = d.main[r] + d.row[0];
+            *(gptr<u32x4>)(run0 + lane * 16u) = c0;
+            *(gptr<u32x4>)(run0 + 1024u + lane * 16u) = c1;
+            if (lane < 36u) *(gptr<u32x4>)(run0 + 2048u + lane * 16u) = c2;
         }
-    }
-    if (d.ok_r) {
+    } else {
+        // A tile's scale is the same in all 16 lanes of its row; the 16 lanes
+        // store it to the same word, which the memory pipeline merges.
 #pragma unroll
-        for (int r = 0; r < R; ++r) *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(d.main[r] + d.rope) = G.rp;
+        for (int k = 0; k < 4; ++k) {
+            if (!((d.tok >> k) & 1u)) continue;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                gbyte* row = d.main[r] + d.row[k];
+                *(gptr<u32x2>)(row + lane * 8u) = codes[k];
+                *(gptr<uint32_t>)(row + 512u + (lane >> 4) * 4u) = __float_as_uint(scale[k]);
+            }
+        }
+        if (d.ok_r) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) *(gptr<u32x4>)(d.main[r] + d.rope) = G.rp;
+        }
     }
     if (d.ok_g) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            *reinterpret_cast<__attribute__((address_space(1))) u32x2*>(d.idx[r] + d.icode) = codes[4];
-            *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(d.idx[r] + d.iscale) =
-                __float_as_uint(scale[4]);
+            *(gptr<u32x2>)(d.idx[r] + d.icode) = codes[4];
+            *(gptr<uint32_t>)(d.idx[r] + d.iscale) = __float_as_uint(scale[4]);
         }
     }
 }
@@ -308,10 +354,11 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d,
 // preloading); p is fetched while the row loads are in flight.  Token
 // indices are 32-bit (a launch holds at most kMaxTokensPerLaunch tokens).
 template <int R>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
+__global__ __launch_bounds__(kWavesPerBlock * 64, KVPUB_MIN_WAVES) void store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
     uint32_t indexer_stride, const uint32_t* __restrict__ status, const StoreParams p) {
+    __shared__ __attribute__((aligned(16))) uint8_t run_img[kWavesPerBlock][kRunBytes];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t num_blocks = (num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;   // == gridDim.x
@@ -350,7 +397,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     if (nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
     const Dest<R> d = destinations<R>(sl[0], sl[1], sl[2], sl[3], poisoned, lane, p);
     __builtin_amdgcn_sched_barrier(0);
-    quantize_store<R>(G, d, lane);
+    quantize_store<R>(G, d, lane, (lbyte*)&run_img[wave][0]);
 }
 
 }  // namespace
