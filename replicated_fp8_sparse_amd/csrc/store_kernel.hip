@@ -49,9 +49,6 @@ typedef __attribute__((address_space(3))) uint8_t lbyte;   // a byte in LDS
 template <class T> using gptr = __attribute__((address_space(1))) T*;
 template <class T> using lptr = __attribute__((address_space(3))) T*;
 
-#ifndef KVPUB_MIN_WAVES
-#define KVPUB_MIN_WAVES 1   // minimum resident waves per SIMD the register budget must allow
-#endif
 #ifndef KVPUB_ROW_RUN
 #define KVPUB_ROW_RUN 1   // assemble runs of 4 consecutive rows in LDS and store them whole
 #endif
@@ -172,10 +169,14 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 
 // Where a group's pieces go, worked out from the slots while its rows are in
 // flight.  Offsets are bytes from a replica's layer base.
+// Replica layer bases, held in SGPRs for the whole wave.
 template <int R>
-struct Dest {
-    gbyte* main[R];    // replica layer bases
+struct Bases {
+    gbyte* main[R];
     gbyte* idx[R];
+};
+
+struct Dest {
     uint64_t row[4];   // Main-KV row of token k (wave-uniform)
     uint32_t tok;      // bit k: token k is stored (wave-uniform)
     uint64_t rope;     // this lane's RoPE piece (lanes 0..31)
@@ -208,7 +209,17 @@ __device__ __forceinline__ gbyte* pin_ptr(uint8_t* v) {
 }
 
 template <int R>
-__device__ __forceinline__ Dest<R> destinations(int64_t s0, int64_t s1, int64_t s2, int64_t s3, bool poisoned,
+__device__ __forceinline__ Bases<R> pin_bases(const StoreParams& p) {
+    Bases<R> b;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        b.main[i] = pin_ptr(p.main_base[i]);
+        b.idx[i] = pin_ptr(p.idx_base[i]);
+    }
+    return b;
+}
+
+__device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2, int64_t s3, bool poisoned,
                                              uint32_t lane, const StoreParams& p) {
     const int64_t sl[4] = {s0, s1, s2, s3};
     uint64_t row[4], irow[4], iscl[4];
@@ -222,12 +233,7 @@ __device__ __forceinline__ Dest<R> destinations(int64_t s0, int64_t s1, int64_t 
         tok |= (!poisoned && slot_ok(sl[k], p.capacity)) ? (1u << k) : 0u;
     }
     const uint32_t g = lane >> 4, r = (lane >> 3) & 3u;
-    Dest<R> d;
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-        d.main[i] = pin_ptr(p.main_base[i]);
-        d.idx[i] = pin_ptr(p.idx_base[i]);
-    }
+    Dest d;
 #pragma unroll
     for (int k = 0; k < 4; ++k) d.row[k] = row[k];
     tok = __builtin_amdgcn_readfirstlane(tok);   // uniform; computed once, before the wait
@@ -255,7 +261,8 @@ __device__ __forceinline__ Dest<R> destinations(int64_t s0, int64_t s1, int64_t 
 // The five rounds are computed as one straight-line block (their reductions
 // and scale sequences interleave); only the stores are conditional.
 template <int R>
-__device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d, uint32_t lane, lbyte* img) {
+__device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, const Bases<R>& b, uint32_t lane,
+                                               lbyte* img) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
 #pragma unroll
@@ -316,7 +323,7 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d,
         const u32x4 c2 = lane < 36u ? *(lptr<u32x4>)(img + 2048u + lane * 16u) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            gbyte* run0 = d.main[r] + d.row[0];
+            gbyte* run0 = b.main[r] + d.row[0];
             *(gptr<u32x4>)(run0 + lane * 16u) = c0;
             *(gptr<u32x4>)(run0 + 1024u + lane * 16u) = c1;
             if (lane < 36u) *(gptr<u32x4>)(run0 + 2048u + lane * 16u) = c2;
@@ -329,23 +336,48 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d,
             if (!((d.tok >> k) & 1u)) continue;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                gbyte* row = d.main[r] + d.row[k];
+                gbyte* row = b.main[r] + d.row[k];
                 *(gptr<u32x2>)(row + lane * 8u) = codes[k];
                 *(gptr<uint32_t>)(row + 512u + (lane >> 4) * 4u) = __float_as_uint(scale[k]);
             }
         }
         if (d.ok_r) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) *(gptr<u32x4>)(d.main[r] + d.rope) = G.rp;
+            for (int r = 0; r < R; ++r) *(gptr<u32x4>)(b.main[r] + d.rope) = G.rp;
         }
     }
     if (d.ok_g) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            *(gptr<u32x2>)(d.idx[r] + d.icode) = codes[4];
-            *(gptr<uint32_t>)(d.idx[r] + d.iscale) = __float_as_uint(scale[4]);
+            *(gptr<u32x2>)(b.idx[r] + d.icode) = codes[4];
+            *(gptr<uint32_t>)(b.idx[r] + d.iscale) = __float_as_uint(scale[4]);
         }
     }
+}
+
+// Slots of the group starting at token t0 (scalar loads).  Token indices
+// past the end are clamped to the last token (always in bounds).
+__device__ __forceinline__ void fetch_slots(const int64_t* __restrict__ slots, uint32_t t0, uint32_t last,
+                                            int64_t (&sl)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sl[k] = slots[t0 + k < last ? t0 + k : last];
+}
+
+// Row loads of the group starting at token t0, in order of first use: the
+// RoPE piece (stored unchanged) first, so that no wait for it lands among the
+// stores, where it would also wait for every store issued before it.
+__device__ __forceinline__ void fetch_rows(const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
+                                           uint32_t latent_stride, uint32_t rope_stride, uint32_t indexer_stride,
+                                           uint32_t t0, uint32_t last, uint32_t lane, Group& G) {
+    const uint32_t ug = t0 + (lane >> 4), ur = t0 + ((lane >> 3) & 3u);
+    const uint32_t tg = ug < last ? ug : last, tr = ur < last ? ur : last;
+    G.rp = ld16(rope + (uint64_t)tr * rope_stride + (lane & 7u) * 8u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t t = t0 + k < last ? t0 + k : last;
+        G.lat[k] = ld16(latent + (uint64_t)t * latent_stride + lane * 8u);
+    }
+    G.ix = ld16(indexer + (uint64_t)tg * indexer_stride + (lane & 15u) * 8u);
 }
 
 // One group per wave; blocks are mapped XCD-aware so that neighbouring
@@ -354,7 +386,7 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<R>& d,
 // preloading); p is fetched while the row loads are in flight.  Token
 // indices are 32-bit (a launch holds at most kMaxTokensPerLaunch tokens).
 template <int R>
-__global__ __launch_bounds__(kWavesPerBlock * 64, KVPUB_MIN_WAVES) void store_kernel(
+__global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
     uint32_t indexer_stride, const uint32_t* __restrict__ status, const StoreParams p) {
@@ -365,39 +397,28 @@ __global__ __launch_bounds__(kWavesPerBlock * 64, KVPUB_MIN_WAVES) void store_ke
     const uint32_t t0 = (xcd_chunk(blockIdx.x, num_blocks) * kWavesPerBlock + wave) * kTokensPerWave;
     if (t0 >= num_tokens) return;
     const uint32_t last = num_tokens - 1;
-    // Scalar loads (slots of the 4 tokens, the status word) do not share a
-    // counter with the row loads, so the destinations are worked out before
-    // the rows arrive.  Token indices past the end are clamped to the last
-    // token (always in bounds); their slots become -1.
+    // Scalar loads (slots, the status word) do not share a counter with the
+    // row loads, so the destinations are worked out before the rows arrive.
     int64_t sl[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sl[k] = slots[t0 + k < last ? t0 + k : last];
+    fetch_slots(slots, t0, last, sl);
     const uint32_t st = *status;
-    // Row loads in order of first use: the RoPE piece (stored unchanged)
-    // first, so that no wait for it lands among the stores, where it would
-    // also wait for every store issued before it.
     Group G;
-    const uint32_t ug = t0 + (lane >> 4), ur = t0 + ((lane >> 3) & 3u);
-    const uint32_t tg = ug < last ? ug : last, tr = ur < last ? ur : last;
-    G.rp = ld16(rope + (uint64_t)tr * rope_stride + (lane & 7u) * 8u);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t t = t0 + k < last ? t0 + k : last;
-        G.lat[k] = ld16(latent + (uint64_t)t * latent_stride + lane * 8u);
-    }
-    G.ix = ld16(indexer + (uint64_t)tg * indexer_stride + (lane & 15u) * 8u);
+    fetch_rows(latent, rope, indexer, latent_stride, rope_stride, indexer_stride, t0, last, lane, G);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sl[k] = t0 + k <= last ? sl[k] : -1;
     const bool poisoned = (st & kStatusPoisoned) != 0;  // a fence timed out: fail closed
-    // Invalid (neither -1 nor a slot of the cache) slots are skipped and counted.
+    // Slots of tokens past the end become -1; invalid slots (neither -1 nor a
+    // slot of the cache) are skipped and counted.
     uint32_t nbad = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) nbad += (sl[k] != -1 && !slot_ok(sl[k], p.capacity)) ? 1u : 0u;
+    for (int k = 0; k < 4; ++k) {
+        sl[k] = t0 + k <= last ? sl[k] : -1;
+        nbad += (sl[k] != -1 && !slot_ok(sl[k], p.capacity)) ? 1u : 0u;
+    }
     if (nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
-    const Dest<R> d = destinations<R>(sl[0], sl[1], sl[2], sl[3], poisoned, lane, p);
+    const Bases<R> b = pin_bases<R>(p);
+    const Dest d = destinations(sl[0], sl[1], sl[2], sl[3], poisoned, lane, p);
     __builtin_amdgcn_sched_barrier(0);
-    quantize_store<R>(G, d, lane, (lbyte*)&run_img[wave][0]);
+    quantize_store<R>(G, d, b, lane, (lbyte*)&run_img[wave][0]);
 }
 
 }  // namespace
