@@ -193,8 +193,10 @@ def main():
     assert invalid == 0 and flags == 0
 
     extras = {}
+    decode = None
     if not args.no_extras:
         extras = store_only_extras(torch, kvpub, W, stream)
+        decode = decode_eager(torch, kvpub, W, stream)
 
     result = {
         "metric": "cache-store tokens/sec and achieved HBM GB/s (% of peak); fence µs/layer",
@@ -239,6 +241,8 @@ def main():
     }
     if extras:
         result["store_only"] = extras
+    if decode:
+        result["decode_store_fence"] = decode
 
     kvpub.kvpub_graph_destroy(graph)
 
@@ -285,48 +289,136 @@ def store_only_extras(torch, kvpub, W, stream):
             for i in range(n):
                 launch(i % copies)
         us = tm.ms * 1e3 / n
+        cold = cold_launch_us(torch, stream, launch, copies)
         b = alg_bytes(valid, R)
         out[name] = {"avg_launch_us": round(us, 3), "alg_bytes": b,
                      "gbps": round(b / (us * 1e-6) / 1e9, 1),
                      "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "tokens_per_s": round(valid / (us * 1e-6), 1)}
+                     "tokens_per_s": round(valid / (us * 1e-6), 1),
+                     "cold_launch_us": round(cold, 3),
+                     "cold_frac": round(b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "how": "warm: back-to-back launches over rotated input copies; cold: each launch "
+                            "timed alone after writing a 1 GiB scratch buffer (flushes L2 and the "
+                            "256 MB memory-side cache)"}
         kvpub.check(kvpub.kvpub_destroy(ctx))
         del mb, ib, lat, rope, idx
         torch.cuda.empty_cache()
     return out
 
 
+def cold_launch_us(torch, stream, launch, copies, n=12):
+    """Median duration of single store launches, each after a 1 GiB scratch write."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    times = []
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            scratch.fill_(i & 0xFF)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch(i % copies)
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+    del scratch
+    torch.cuda.empty_cache()
+    return float(np.median(times))
+
+
+def decode_eager(torch, kvpub, W, stream):
+    """The decode shape (61 layers x T=64, R=2, 4096 pages): eager store + fence per
+    layer, for context (a latency-bound case)."""
+    layout, xs = W.decode()
+    R = layout.replicas
+    sh = stream.cuda_stream
+    mb = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    ib = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    for b in mb:
+        layout.fill_device(b, "main")
+    for b in ib:
+        layout.fill_device(b, "idx")
+    cfg = kvpub.kvpub_config_init(R, layout.layers, layout.num_pages)
+    st, ctx = kvpub.kvpub_create(cfg, [b.data_ptr() for b in mb], [b.data_ptr() for b in ib])
+    kvpub.check(st)
+    dev = []
+    for x in xs:
+        dev.append((torch.from_numpy(x.latent.view(np.int16)).to("cuda"),
+                    torch.from_numpy(x.rope.view(np.int16)).to("cuda"),
+                    torch.from_numpy(x.indexer.view(np.int16)).to("cuda"),
+                    torch.from_numpy(x.slots).to("cuda")))
+    T = xs[0].slots.size
+
+    def one_pass():
+        for l, (a, r, i, s_) in enumerate(dev):
+            kvpub.kvpub_store(ctx, l, T, a.data_ptr(), 512, r.data_ptr(), 64, i.data_ptr(), 128,
+                              s_.data_ptr(), sh)
+            kvpub.kvpub_fence(ctx, 0, sh)
+
+    one_pass()
+    reps = 5
+    with Timer(torch, stream) as tm:
+        for _ in range(reps):
+            one_pass()
+    kvpub.check(kvpub.kvpub_destroy(ctx))
+    del mb, ib, dev
+    torch.cuda.empty_cache()
+    return {"us_per_layer": round(tm.ms * 1e3 / (reps * len(xs)), 3),
+            "how": "eager kvpub_store + kvpub_fence per layer, 61 layers x T=64, R=2, 4096 pages; "
+                   "includes host launch cost"}
+
+
 def cpu_baseline(lat, rope, idx, slots_np, layout, seconds):
-    """The CPU oracle (single-threaded C, as it stands) on a bounded sample of the
-    same workload: the graph workload's layers one after another, into host
-    replicas of one layer-cache, until about `seconds` of CPU time."""
+    """The CPU oracle (plain C, as it stands) on a bounded sample of the same workload:
+    the graph workload's layers one after another, into host replicas of one
+    layer-cache, until about `seconds` of wall time per leg.  Timed single-threaded
+    and with one thread per host core (at most 16) over contiguous token ranges of
+    each layer (race-free: the valid slots of a layer are distinct; the C calls
+    release the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     orc = oracle.get()
     L = lat.shape[0]
     m0, i0 = oracle_host_layer(layout)
     mains = [m0.copy() for _ in range(layout.replicas)]
     idxs = [i0.copy() for _ in range(layout.replicas)]
-    done_tokens = 0
-    elapsed = 0.0
-    layers = 0
-    for l in range(L):
-        x_l = lat[l].cpu().view(torch_int16()).numpy().view(np.uint16)
-        x_r = rope[l].cpu().view(torch_int16()).numpy().view(np.uint16)
-        x_i = idx[l].cpu().view(torch_int16()).numpy().view(np.uint16)
-        t0 = time.perf_counter()
+    valid_per_layer = int(((slots_np >= 0) & (slots_np < layout.capacity)).sum())
+    T = slots_np.size
+
+    def store_range(x_l, x_r, x_i, a, b):
         orc.store(mains, idxs, num_pages=layout.num_pages,
                   main_page_stride=layout.main_page_stride, main_layer_stride=layout.main_layer_stride,
                   idx_page_stride=layout.idx_page_stride, idx_layer_stride=layout.idx_layer_stride,
-                  layer=0, latent=x_l, rope=x_r, indexer=x_i, slot_mapping=slots_np)
-        elapsed += time.perf_counter() - t0
-        done_tokens += int(((slots_np >= 0) & (slots_np < layout.capacity)).sum())
-        layers += 1
-        if elapsed >= seconds:
-            break
-    return {"value": round(done_tokens / elapsed, 1), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{layers} layers of the graph workload (T=4096, R=2, 8192 pages), "
-                      f"single-threaded C oracle, {elapsed:.1f} s",
+                  layer=0, latent=x_l[a:b], rope=x_r[a:b], indexer=x_i[a:b], slot_mapping=slots_np[a:b])
+
+    def leg(threads, budget):
+        done, elapsed, layers = 0, 0.0, 0
+        bounds = np.linspace(0, T, threads + 1).astype(int)
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            for l in range(L):
+                x_l = lat[l].cpu().view(torch_int16()).numpy().view(np.uint16)
+                x_r = rope[l].cpu().view(torch_int16()).numpy().view(np.uint16)
+                x_i = idx[l].cpu().view(torch_int16()).numpy().view(np.uint16)
+                t0 = time.perf_counter()
+                if threads == 1:
+                    store_range(x_l, x_r, x_i, 0, T)
+                else:
+                    list(ex.map(lambda ab: store_range(x_l, x_r, x_i, ab[0], ab[1]),
+                                zip(bounds[:-1], bounds[1:])))
+                elapsed += time.perf_counter() - t0
+                done += valid_per_layer
+                layers += 1
+                if elapsed >= budget:
+                    break
+        return done / elapsed, layers, elapsed
+
+    one, l1, e1 = leg(1, seconds / 2)
+    cores = max(1, min(os.cpu_count() or 1, 16))
+    many, lm, em = leg(cores, seconds / 2) if cores > 1 else (one, l1, e1)
+    return {"value": round(many, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"graph workload layers (T=4096, R=2, 8192 pages) through the C oracle: "
+                      f"{lm} layers on {cores} threads in {em:.1f} s; single-threaded "
+                      f"{l1} layers in {e1:.1f} s",
+            "single_thread_value": round(one, 1),
             "host_cpus": os.cpu_count()}
 
 
