@@ -53,6 +53,18 @@ template <class T> using lptr = __attribute__((address_space(3))) T*;
 #define KVPUB_ROW_RUN 1   // assemble runs of 4 consecutive rows in LDS and store them whole
 #endif
 constexpr uint32_t kRunBytes = 4 * 656;   // 2624 = 164 x 16 B
+constexpr int64_t kCacheBytesPerToken = 656 + 128 + 4;              // per replica
+constexpr int64_t kStreamingStoreBytes = int64_t(16) << 20;         // launches writing at most this stream
+
+// Whole-line pieces (row runs, Indexer-K codes) of a small launch are stored
+// non-temporally: nothing of them is left dirty in L2 for the end-of-kernel
+// write-back, which a latency-bound launch would otherwise wait for.  Large
+// launches keep write-back stores, whose merging in L2 pays at full bandwidth.
+template <bool NT, class T>
+__device__ __forceinline__ void put(gptr<T> p, T v) {
+    if (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 constexpr float kE4m3Max = 448.0f;
 constexpr int kNumXcds = 8;
@@ -260,7 +272,7 @@ __device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2,
 //   Indexer-K scale   -> page bytes [8192 + 4*(slot%64), +4) (lane 16g)
 // The five rounds are computed as one straight-line block (their reductions
 // and scale sequences interleave); only the stores are conditional.
-template <int R>
+template <int R, bool NT>
 __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, const Bases<R>& b, uint32_t lane,
                                                lbyte* img) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
@@ -324,9 +336,9 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, co
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             gbyte* run0 = b.main[r] + d.row[0];
-            *(gptr<u32x4>)(run0 + lane * 16u) = c0;
-            *(gptr<u32x4>)(run0 + 1024u + lane * 16u) = c1;
-            if (lane < 36u) *(gptr<u32x4>)(run0 + 2048u + lane * 16u) = c2;
+            put<NT>((gptr<u32x4>)(run0 + lane * 16u), c0);
+            put<NT>((gptr<u32x4>)(run0 + 1024u + lane * 16u), c1);
+            if (lane < 36u) put<NT>((gptr<u32x4>)(run0 + 2048u + lane * 16u), c2);
         }
     } else {
         // A tile's scale is the same in all 16 lanes of its row; the 16 lanes
@@ -349,7 +361,7 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, co
     if (d.ok_g) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            *(gptr<u32x2>)(b.idx[r] + d.icode) = codes[4];
+            put<NT>((gptr<u32x2>)(b.idx[r] + d.icode), codes[4]);
             *(gptr<uint32_t>)(b.idx[r] + d.iscale) = __float_as_uint(scale[4]);
         }
     }
@@ -385,7 +397,7 @@ __device__ __forceinline__ void fetch_rows(const uint16_t* latent, const uint16_
 // instructions need: they arrive preloaded in SGPRs (kernel-argument
 // preloading); p is fetched while the row loads are in flight.  Token
 // indices are 32-bit (a launch holds at most kMaxTokensPerLaunch tokens).
-template <int R>
+template <int R, bool NT>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
@@ -418,10 +430,28 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const Bases<R> b = pin_bases<R>(p);
     const Dest d = destinations(sl[0], sl[1], sl[2], sl[3], poisoned, lane, p);
     __builtin_amdgcn_sched_barrier(0);
-    quantize_store<R>(G, d, b, lane, (lbyte*)&run_img[wave][0]);
+    quantize_store<R, NT>(G, d, b, lane, (lbyte*)&run_img[wave][0]);
 }
 
 }  // namespace
+
+template <bool NT>
+static void launch_r(uint32_t num_replicas, dim3 grid, dim3 block, hipStream_t stream, const uint16_t* lat,
+                     const uint16_t* rp, const uint16_t* ix, const int64_t* sl, uint32_t n, const StoreParams& p) {
+#define KVPUB_ROW_ARGS lat, rp, ix, sl, n, (uint32_t)p.latent_stride, (uint32_t)p.rope_stride, \
+    (uint32_t)p.indexer_stride, p.status, p
+    switch (num_replicas) {
+        case 1: store_kernel<1, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 2: store_kernel<2, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 3: store_kernel<3, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 4: store_kernel<4, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 5: store_kernel<5, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 6: store_kernel<6, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 7: store_kernel<7, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        default: store_kernel<8, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+    }
+#undef KVPUB_ROW_ARGS
+}
 
 hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream) {
     if (num_replicas < 1 || num_replicas > (uint32_t)kMaxReplicas) return hipErrorInvalidValue;
@@ -436,19 +466,9 @@ hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t
         const uint16_t* rp = p.rope + t * p.rope_stride;
         const uint16_t* ix = p.indexer + t * p.indexer_stride;
         const int64_t* sl = p.slots + t;
-#define KVPUB_ROW_ARGS lat, rp, ix, sl, (uint32_t)n, (uint32_t)p.latent_stride, (uint32_t)p.rope_stride, \
-    (uint32_t)p.indexer_stride, p.status, p
-        switch (num_replicas) {
-            case 1: store_kernel<1><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-            case 2: store_kernel<2><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-            case 3: store_kernel<3><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-            case 4: store_kernel<4><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-            case 5: store_kernel<5><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-            case 6: store_kernel<6><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-            case 7: store_kernel<7><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-            default: store_kernel<8><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        }
-#undef KVPUB_ROW_ARGS
+        const bool small = n * (int64_t)num_replicas * kCacheBytesPerToken <= kStreamingStoreBytes;
+        if (small) launch_r<true>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
+        else launch_r<false>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
