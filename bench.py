@@ -221,7 +221,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "store_kernel<2>",
+            "kernel": "store_kernel<2, true>",
             "achieved": round(store_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
