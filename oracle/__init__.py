@@ -54,6 +54,13 @@ class Oracle:
                                   ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32,
                                   ctypes.c_int64, _u16p, ctypes.c_int64, _u16p,
                                   ctypes.c_int64, _u16p, ctypes.c_int64, _i64p]
+        lib.kvo_dequant_tile.restype = None
+        lib.kvo_dequant_tile.argtypes = [_u8p, ctypes.c_float, ctypes.c_size_t, _u16p]
+        lib.kvo_gather.restype = ctypes.c_int64
+        lib.kvo_gather.argtypes = [_u8p, _u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                   ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64,
+                                   _i64p, _u16p, ctypes.c_int64, _u16p, ctypes.c_int64, _u16p,
+                                   ctypes.c_int64]
         lib.kvo_epoch_after.restype = ctypes.c_uint64
         lib.kvo_epoch_after.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
         lib.kvo_plant_id.restype = ctypes.c_int
@@ -124,6 +131,33 @@ class Oracle:
                                       _ptr(rope, _u16p), rope.shape[1] if T else 64,
                                       _ptr(indexer, _u16p), indexer.shape[1] if T else 128,
                                       _ptr(slots, _i64p)))
+
+    # -- the reader ---------------------------------------------------
+    def dequant_tile(self, codes, scale):
+        """codes: uint8 array (any length) sharing one fp32 scale -> bf16 bit patterns."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.uint16)
+        self.lib.kvo_dequant_tile(_ptr(c, _u8p), float(np.float32(scale)), c.size, _ptr(out, _u16p))
+        return out
+
+    def gather(self, main_replica, idx_replica, *, num_pages, main_page_stride, main_layer_stride,
+               idx_page_stride, idx_layer_stride, layer, slot_mapping):
+        """Dequantizing gather from one host replica: (latent [T,512], rope [T,64], indexer [T,128])
+        as bf16 bit patterns (uint16), and the number of out-of-range slots."""
+        for b in (main_replica, idx_replica):
+            assert b.dtype == np.uint8 and b.flags.c_contiguous
+        slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        T = slots.shape[0]
+        assert main_replica.size >= layer * main_layer_stride + num_pages * main_page_stride
+        assert idx_replica.size >= layer * idx_layer_stride + num_pages * idx_page_stride
+        lat = np.empty((T, 512), dtype=np.uint16)
+        rope = np.empty((T, 64), dtype=np.uint16)
+        idx = np.empty((T, 128), dtype=np.uint16)
+        bad = self.lib.kvo_gather(_ptr(main_replica, _u8p), _ptr(idx_replica, _u8p), num_pages,
+                                  main_page_stride, main_layer_stride, idx_page_stride,
+                                  idx_layer_stride, layer, T, _ptr(slots, _i64p),
+                                  _ptr(lat, _u16p), 512, _ptr(rope, _u16p), 64, _ptr(idx, _u16p), 128)
+        return lat, rope, idx, int(bad)
 
     def epoch_after(self, e0, n_fences):
         return int(self.lib.kvo_epoch_after(e0, n_fences))

@@ -352,6 +352,134 @@ int64_t kvo_store(uint32_t num_replicas,
     return invalid;
 }
 
+/* ------------------------------------------------------------------ */
+/* the reader: dequantizing gather from one replica                     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * What the attention side reads back from a replica (vLLM PR #52863,
+ * Summary and Design: the existing attention kernels keep reading the local
+ * replica, in the fp8_ds_mla layout this path writes).  Readings taken here:
+ *   - element k of a tile = bf16(RN32(value(code_k) * scale)): the e4m3 value
+ *     (exact in binary32) times the tile's fp32 scale, rounded once to
+ *     binary32, then rounded to bf16 (nearest, ties to even);
+ *   - RoPE: the 64 stored bf16 values, bit for bit;
+ *   - a padded (-1) or out-of-range slot gives an all-zero output row; the
+ *     out-of-range ones are counted, as in the store.
+ */
+static uint32_t get_le32(const uint8_t *src)
+{
+    return (uint32_t)src[0] | ((uint32_t)src[1] << 8) | ((uint32_t)src[2] << 16)
+           | ((uint32_t)src[3] << 24);
+}
+
+static float float_from_bits(uint32_t u)
+{
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Signed value of the e4m3 code c (0x7F / 0xFF, NaN, are never stored). */
+static double e4m3_value(uint8_t c)
+{
+#if defined(KVO_PLANT) && KVO_PLANT == 14
+    return e4m3_magnitude(c & 0x7Fu);               /* planted: sign dropped on decode */
+#else
+    double m = e4m3_magnitude(c & 0x7Fu);
+    return (c & 0x80u) ? -m : m;
+#endif
+}
+
+/*
+ * binary32 -> bf16, round to nearest, ties to even: of the two bf16 values
+ * around v (t = v with its low 16 bits cleared, and the next bf16 away from
+ * zero) take the nearer; on a tie the one with an even bit pattern.  The
+ * distances are exact in binary64.  Finite input only.
+ */
+static uint16_t float_to_bf16(float v)
+{
+    uint16_t t = (uint16_t)(float_bits(v) >> 16);
+    double lo = (double)bf16_to_float(t), hi = (double)bf16_to_float((uint16_t)(t + 1u));
+    double dl = (double)v - lo, dh = hi - (double)v;
+    if (dl < 0) dl = -dl;
+    if (dh < 0) dh = -dh;
+#if defined(KVO_PLANT) && KVO_PLANT == 15
+    return t;                                        /* planted: truncation */
+#endif
+    if (dl < dh) return t;
+    if (dh < dl) return (uint16_t)(t + 1u);
+    return (t & 1u) ? (uint16_t)(t + 1u) : t;
+}
+
+/* n codes sharing one scale -> n bf16 values. */
+void kvo_dequant_tile(const uint8_t *codes, float scale, size_t n, uint16_t *out)
+{
+    size_t k;
+    for (k = 0; k < n; ++k) {
+        float v = (float)e4m3_value(codes[k]);       /* exact */
+        float p = v * scale;                          /* one binary32 rounding */
+        out[k] = float_to_bf16(p);
+    }
+}
+
+/*
+ * Gather tokens t = 0..T-1 from one replica (bases already at the replica;
+ * same strides as kvo_store): latent_out[t][0..511], rope_out[t][0..63] and
+ * indexer_out[t][0..127] (bf16 bit patterns, row strides in elements).
+ * Returns the number of out-of-range slots (not -1).
+ */
+int64_t kvo_gather(const uint8_t *main_base, const uint8_t *idx_base, uint64_t num_pages,
+                   uint64_t main_page_stride, uint64_t main_layer_stride,
+                   uint64_t idx_page_stride, uint64_t idx_layer_stride,
+                   uint32_t layer, int64_t num_tokens, const int64_t *slot_mapping,
+                   uint16_t *latent_out, int64_t latent_stride,
+                   uint16_t *rope_out, int64_t rope_stride,
+                   uint16_t *indexer_out, int64_t indexer_stride)
+{
+    const int64_t capacity = (int64_t)(num_pages * KVO_SLOTS_PER_PAGE);
+    int64_t invalid = 0, t;
+    int j, k;
+
+    for (t = 0; t < num_tokens; ++t) {
+        int64_t s = slot_mapping[t];
+        uint16_t *lo = latent_out + t * latent_stride;
+        uint16_t *ro = rope_out + t * rope_stride;
+        uint16_t *io = indexer_out + t * indexer_stride;
+        const uint8_t *row, *ipage;
+        uint64_t page, off;
+        if (s != -1 && (s < 0 || s >= capacity)) ++invalid;
+        if (s < 0 || s >= capacity) {                /* padded or out of range: zeros */
+            memset(lo, 0, KVO_LATENT * sizeof *lo);
+            memset(ro, 0, KVO_ROPE * sizeof *ro);
+            memset(io, 0, KVO_INDEXER * sizeof *io);
+            continue;
+        }
+        page = (uint64_t)s / KVO_SLOTS_PER_PAGE;
+        off = (uint64_t)s % KVO_SLOTS_PER_PAGE;
+        row = main_base + (uint64_t)layer * main_layer_stride + page * main_page_stride
+              + off * KVO_MAIN_ROW_BYTES;
+        ipage = idx_base + (uint64_t)layer * idx_layer_stride + page * idx_page_stride;
+        for (j = 0; j < KVO_LATENT / KVO_TILE; ++j) {
+#if defined(KVO_PLANT) && KVO_PLANT == 16
+            float scale = float_from_bits(get_le32(row + KVO_LATENT + 4 * ((j + 1) % 4)));  /* planted */
+#else
+            float scale = float_from_bits(get_le32(row + KVO_LATENT + 4 * j));
+#endif
+            kvo_dequant_tile(row + j * KVO_TILE, scale, KVO_TILE, lo + j * KVO_TILE);
+        }
+        for (k = 0; k < KVO_ROPE; ++k) {
+            const uint8_t *b = row + KVO_LATENT + 16 + 2 * k;
+            ro[k] = (uint16_t)(b[0] | (b[1] << 8));
+        }
+        kvo_dequant_tile(ipage + off * KVO_IDX_CODES_BYTES,
+                         float_from_bits(get_le32(ipage + KVO_SLOTS_PER_PAGE * KVO_IDX_CODES_BYTES
+                                                  + off * 4)),
+                         KVO_INDEXER, io);
+    }
+    return invalid;
+}
+
 /* Epoch after n fence executions starting from e0: each advances it by one. */
 uint64_t kvo_epoch_after(uint64_t e0, uint64_t n_fences)
 {

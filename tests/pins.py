@@ -18,6 +18,11 @@ from the oracle itself:
   every byte outside the written rows unchanged, invalid slots counted,
   token order irrelevant, R replicas == R single-replica inserts.
 
+* the reader side (dequantizing gather): hand-derived products and their
+  bf16 rounding (``golden/gather_hand_values.txt``), a bit-exact round trip of
+  tiles whose values and scales are exact, the half-step error bound on random
+  rows, zero rows for padded and out-of-range slots.
+
 ``tests/test_oracle_plants.py`` builds copies of the oracle with planted
 mistakes and checks that at least one pin fails for each.
 """
@@ -437,6 +442,95 @@ def pin_store_empty(orc):
     assert n == 0 and np.array_equal(before, cache.main[0])
 
 
+# ---------------------------------------------------------------------------
+# reader-side pins (dequantizing gather)
+# ---------------------------------------------------------------------------
+
+def load_gather_hand_values():
+    rows = []
+    with open(os.path.join(GOLDEN, "gather_hand_values.txt")) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, s, b = line.split()[:3]
+            rows.append((int(c, 16), np.array([int(s, 16)], np.uint32).view(np.float32)[0], int(b, 16)))
+    return rows
+
+
+def pin_gather_hand_values(orc):
+    for code, scale, want in load_gather_hand_values():
+        got = int(orc.dequant_tile(np.array([code], np.uint8), scale)[0])
+        assert got == want, f"dequant {code:#04x} * {float(scale)!r}: {got:#06x} != {want:#06x}"
+
+
+def _gather(orc, cache, layer, slots, r=0):
+    return orc.gather(cache.main[r], cache.idx[r], num_pages=cache.pages, main_page_stride=cache.mps,
+                      main_layer_stride=cache.mls, idx_page_stride=cache.ips, idx_layer_stride=cache.ils,
+                      layer=layer, slot_mapping=slots)
+
+
+def pin_gather_roundtrip_exact(orc):
+    """Tiles of e4m3 values with amax 448 * 2^k: the scale is exactly 2^k, every
+    quotient is exactly representable, and value * 2^k is exact in bf16 (4
+    significant bits), so store followed by gather must give back the input bits."""
+    rng = np.random.default_rng(21)
+    T = 64
+    grid = np.array([c for c in range(0x7F) if c != 0], np.uint8)
+    vals = e4m3_decode(grid)
+    lat = np.empty((T, 512), np.float64)
+    idx = np.empty((T, 128), np.float64)
+    for t in range(T):
+        for j in range(4):
+            k = int(rng.integers(-20, 21))
+            v = rng.choice(vals, 128) * rng.choice([-1.0, 1.0], 128)
+            v[int(rng.integers(0, 128))] = 448.0 * (1 if rng.random() < 0.5 else -1)
+            lat[t, 128 * j:128 * (j + 1)] = v * 2.0 ** k
+        k = int(rng.integers(-20, 21))
+        v = rng.choice(vals, 128)
+        v[0] = 448.0
+        idx[t] = v * 2.0 ** k
+    latent = f32_to_bf16_rne(lat.astype(np.float32))
+    indexer = f32_to_bf16_rne(idx.astype(np.float32))
+    assert np.array_equal(bf16_to_f32(latent).astype(np.float64), lat)        # exact in bf16
+    rope = f32_to_bf16_rne(rng.standard_normal((T, 64)).astype(np.float32))
+    cache = SmallCache(R=1, pages=4)
+    slots = rng.permutation(4 * 64)[:T].astype(np.int64)
+    cache.store(orc, 0, latent, rope, indexer, slots)
+    g_lat, g_rope, g_idx, bad = _gather(orc, cache, 0, slots)
+    assert bad == 0
+    assert np.array_equal(g_lat, latent), "exact tiles do not round-trip (latent)"
+    assert np.array_equal(g_idx, indexer), "exact tiles do not round-trip (indexer)"
+    assert np.array_equal(g_rope, rope), "RoPE bits not returned verbatim"
+
+
+def pin_gather_bound_and_pads(orc):
+    """Random rows: the gathered value is within half an e4m3 step (at the tile
+    scale) of the input, plus the binary32 and bf16 roundings; padded and
+    out-of-range slots give zero rows, out-of-range ones are counted."""
+    rng = np.random.default_rng(22)
+    T = 160
+    latent, rope, indexer, slots = small_inputs(rng, T, 8 * 64, n_pad=10, n_invalid=3)
+    cache = SmallCache(R=2, pages=8)
+    cache.store(orc, 0, latent, rope, indexer, slots)
+    g_lat, g_rope, g_idx, bad = _gather(orc, cache, 0, slots, r=1)
+    assert bad == 3, f"out-of-range count {bad} != 3"
+    valid = (slots >= 0) & (slots < 8 * 64)
+    assert np.all(g_lat[~valid] == 0) and np.all(g_rope[~valid] == 0) and np.all(g_idx[~valid] == 0), \
+        "padded / out-of-range rows not zero"
+    assert np.array_equal(g_rope[valid], rope[valid]), "RoPE bits not returned verbatim"
+    for x_bits, g_bits, ntile in ((latent, g_lat, 4), (indexer, g_idx, 1)):
+        x = bf16_to_f32(x_bits[valid]).astype(np.float64).reshape(-1, ntile, 128)
+        g = bf16_to_f32(g_bits[valid]).astype(np.float64).reshape(-1, ntile, 128)
+        amax = np.abs(x).max(axis=2, keepdims=True)
+        scale = amax / 448.0
+        # e4m3 half step at the dequantized magnitude, in units of the scale
+        q = np.abs(x) / np.where(scale > 0, scale, 1.0)
+        step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(q, 2.0 ** -6))), -6) - 3)
+        bound = 0.5 * step * scale * (1 + 2.0 ** -20) + np.abs(x) * 2.0 ** -22 + np.abs(g) * 2.0 ** -8
+        assert np.all(np.abs(g - x) <= bound), "gathered value outside the dequantization bound"
+
+
 def pin_epoch(orc):
     assert orc.epoch_after(0, 61 * 100) == 6100
     assert orc.epoch_after(5, 0) == 5
@@ -444,4 +538,5 @@ def pin_epoch(orc):
 
 ALL_PINS = [pin_hand_codes, pin_encoder_bruteforce, pin_encoder_torch, pin_encoder_nearest,
             pin_tile_exact, pin_tile_invariants, pin_tile_nearest, pin_tile_special,
-            pin_layout, pin_layout_order_and_fanout, pin_store_empty, pin_epoch]
+            pin_layout, pin_layout_order_and_fanout, pin_store_empty, pin_epoch,
+            pin_gather_hand_values, pin_gather_roundtrip_exact, pin_gather_bound_and_pads]
