@@ -26,6 +26,11 @@
  *     several layers captured once in a hipGraph and replayed (PR #54030
  *     commit list: a two-GPU replay test checks that every replay advances the
  *     epoch; PR #52863 Design: graph replay is supported).
+ *   - kvpub_gather: the reader side -- the rows of given slots read back from
+ *     one replica and dequantized to bf16, which is what the attention kernels
+ *     that keep reading the local replica consume (PR #52863 Summary and
+ *     Design: the existing attention kernels read the local replica in the
+ *     fp8_ds_mla layout this path writes).
  *   - all-or-nothing creation and fail-closed fences (PR #54030 commit list:
  *     opt-in allocation is all-or-nothing at startup; a fence timeout must not
  *     let work continue).
@@ -151,6 +156,33 @@ KVPUB_API kvpub_status kvpub_store(kvpub_ctx *ctx, uint32_t layer, int64_t num_t
                          const void *rope, int64_t rope_row_stride,
                          const void *indexer, int64_t indexer_row_stride,
                          const int64_t *slot_mapping, kvpub_stream_t stream);
+
+/* Dequantizing gather from replica `replica`, layer `layer`, asynchronously on
+ * `stream` (the reader side of the cache this library writes).  For token t
+ * with slot s = slot_mapping[t]:
+ *   latent_out[t][k]  = bf16(RN32(value(code_k) * scale_(k/128))) for k < 512,
+ *   rope_out[t][k]    = the stored RoPE bits, k < 64,
+ *   indexer_out[t][k] = bf16(RN32(value(icode_k) * iscale)), k < 128,
+ * where value() is the OCP E4M3 value of a stored code, the product is rounded
+ * once to binary32 and then to bf16 (nearest, ties to even).  s == -1 or s
+ * outside [0, num_pages*64) gives all-zero output rows; the out-of-range ones
+ * are added to the context's invalid-slot counter (kvpub_error_read).
+ *   latent_out:  bf16 [T, 512], row stride latent_row_stride elements
+ *   rope_out:    bf16 [T, 64],  row stride rope_row_stride elements
+ *   indexer_out: bf16 [T, 128], row stride indexer_row_stride elements
+ *   slot_mapping: int64 [T] device array
+ * Outputs are caller-owned device buffers, 16-byte aligned, row strides
+ * multiples of 8 elements and at least the row width; slot_mapping is 8-byte
+ * aligned.  Only the output rows are written; the cache is only read.  A
+ * context poisoned by a fence timeout still gathers (reading publishes
+ * nothing).  num_tokens == 0 returns KVPUB_OK and launches nothing.  No
+ * allocation and no synchronization: safe under stream capture.  Argument
+ * problems (replica >= R, layer >= L, bad pointers or strides) return
+ * KVPUB_ERR_INVALID_ARG before anything is launched. */
+KVPUB_API kvpub_status kvpub_gather(kvpub_ctx *ctx, uint32_t replica, uint32_t layer, int64_t num_tokens,
+                                    const int64_t *slot_mapping, void *latent_out, int64_t latent_row_stride,
+                                    void *rope_out, int64_t rope_row_stride, void *indexer_out,
+                                    int64_t indexer_row_stride, kvpub_stream_t stream);
 
 /* One fence on `lane`, asynchronously on `stream`: a single one-wavefront
  * kernel that adds 1 to the lane's device epoch with a system-scope release,

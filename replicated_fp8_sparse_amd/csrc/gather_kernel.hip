@@ -1,0 +1,154 @@
+// Dequantizing gather for gfx950: the reader side of the replicated cache.
+//
+// vLLM PR #52863 "[Kernel][PCP] Publish replicated KV updates through PyTorch
+// symmetric memory", Summary and Design: the existing attention kernels keep
+// reading the local replica, in the fp8_ds_mla layout the store writes.  This
+// kernel reads the rows of given slots from one replica and turns them back
+// into bf16: element = bf16(RN32(value(code) * scale)), RoPE bits copied.
+//
+// Work mapping (wave64), the store's mirror image.  A wave owns 4 consecutive
+// output tokens; a DPP row of 16 lanes x 8 codes (8 bytes per lane) is one
+// 128-element tile:
+//   round k = 0..3: token k's latent, lanes 16j..16j+15 = tile j;
+//   round 4:        the indexer rows, lanes 16g..16g+15 = token g;
+// lanes 0..31 also carry the 4 tokens' RoPE rows (8 lanes x 16 B each).
+// The slots arrive through scalar loads.  A padded or out-of-range slot reads
+// slot 0's bytes (always in bounds, so no load sits behind a branch) and its
+// output row is written as zeros.  Decode: the gfx950 OCP e4m3 -> f32 convert
+// (exact), one binary32 multiply by the tile scale, a round-to-nearest-even
+// f32 -> bf16 convert; each lane stores 8 bf16 = 16 bytes.
+#include "kvpub_internal.h"
+
+namespace kvpub {
+namespace {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <class T> using gptr = __attribute__((address_space(1))) T*;
+template <class T> using cgptr = const __attribute__((address_space(1))) T*;
+
+constexpr int kGatherWaves = 4;                       // waves per block
+constexpr int kGatherTokensPerBlock = 4 * kGatherWaves;
+constexpr int kNumXcds = 8;
+
+// Block b runs on XCD b % 8: give each XCD a contiguous range of token chunks.
+__device__ __forceinline__ uint32_t xcd_chunk(uint32_t b, uint32_t n) {
+    const uint32_t per = n / kNumXcds, rem = n % kNumXcds;
+    const uint32_t x = b % kNumXcds, i = b / kNumXcds;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+// Two bf16 bit patterns (low half first) from two binary32 values, nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// 8 codes (little-endian in c) times one scale -> 8 bf16 in 16 bytes.
+__device__ __forceinline__ u32x4 dequant8(u32x2 c, float scale) {
+    u32x4 r;
+    // the convert's word select picks bytes 0,1 (false) or 2,3 (true) of its source
+    const f32x2 a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false);
+    const f32x2 a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true);
+    const f32x2 b0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false);
+    const f32x2 b1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true);
+    r.x = pack_bf16(a0.x * scale, a0.y * scale);
+    r.y = pack_bf16(a1.x * scale, a1.y * scale);
+    r.z = pack_bf16(b0.x * scale, b0.y * scale);
+    r.w = pack_bf16(b1.x * scale, b1.y * scale);
+    return r;
+}
+
+__device__ __forceinline__ bool slot_ok(int64_t s, int64_t capacity) {
+    return (uint64_t)s < (uint64_t)capacity;   // negative slots wrap to huge values
+}
+
+// v_i for a per-lane index i in 0..3; v0..v3 wave-uniform.
+__device__ __forceinline__ uint64_t pick4(uint64_t v0, uint64_t v1, uint64_t v2, uint64_t v3, uint32_t i) {
+    const uint64_t a = (i & 1u) ? v1 : v0;
+    const uint64_t b = (i & 1u) ? v3 : v2;
+    return (i & 2u) ? b : a;
+}
+
+__global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(const GatherParams p, uint32_t num_blocks) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t t0 = ((int64_t)xcd_chunk(blockIdx.x, num_blocks) * kGatherWaves + wave) * 4;
+    if (t0 >= p.num_tokens) return;
+    const int64_t last = p.num_tokens - 1;
+    int64_t s[4];
+    uint64_t row[4], irow[4], iscl[4];
+    uint32_t ok = 0, nbad = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int64_t t = t0 + k < last ? t0 + k : last;
+        const int64_t v = t0 + k <= last ? p.slots[t] : -1;
+        const bool good = slot_ok(v, p.capacity);
+        nbad += (v != -1 && !good) ? 1u : 0u;
+        ok |= good ? (1u << k) : 0u;
+        s[k] = good ? v : 0;                     // bad slots read slot 0 (in bounds) and emit zeros
+        const uint64_t page = (uint64_t)s[k] >> 6, in = (uint64_t)s[k] & 63u;
+        row[k] = page * p.main_page_stride + in * 656u;
+        irow[k] = page * p.idx_page_stride + in * 128u;
+        iscl[k] = page * p.idx_page_stride + 8192u + in * 4u;
+    }
+    if (nbad != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
+    ok = __builtin_amdgcn_readfirstlane(ok);
+
+    // loads: four latent tiles (codes + the row's scale), the indexer tile, RoPE
+    const uint32_t j = lane >> 4, g = lane >> 4, r = (lane >> 3) & 3u;
+    u32x2 code[5];
+    float scale[5];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint8_t* rw = p.main_base + row[k];
+        code[k] = *(cgptr<u32x2>)(rw + lane * 8u);
+        scale[k] = *(cgptr<float>)(rw + 512u + j * 4u);
+    }
+    const uint64_t my_irow = pick4(irow[0], irow[1], irow[2], irow[3], g);
+    const uint64_t my_iscl = pick4(iscl[0], iscl[1], iscl[2], iscl[3], g);
+    code[4] = *(cgptr<u32x2>)(p.idx_base + my_irow + (lane & 15u) * 8u);
+    scale[4] = *(cgptr<float>)(p.idx_base + my_iscl);
+    const uint64_t my_rope = pick4(row[0], row[1], row[2], row[3], r) + 528u + (lane & 7u) * 16u;
+    const u32x4 rp = *(cgptr<u32x4>)(p.main_base + my_rope);
+
+    // dequantize and store
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (t0 + k > last) break;                // uniform: the tail of the last group
+        const u32x4 v = ((ok >> k) & 1u) ? dequant8(code[k], scale[k]) : zero;
+        *(gptr<u32x4>)(p.latent + (t0 + k) * p.latent_stride + lane * 8u) = v;
+    }
+    if (t0 + g <= last) {
+        const u32x4 v = ((ok >> g) & 1u) ? dequant8(code[4], scale[4]) : zero;
+        *(gptr<u32x4>)(p.indexer + (t0 + g) * p.indexer_stride + (lane & 15u) * 8u) = v;
+    }
+    if (lane < 32u && t0 + r <= last) {
+        const u32x4 v = ((ok >> r) & 1u) ? rp : zero;
+        *(gptr<u32x4>)(p.rope + (t0 + r) * p.rope_stride + (lane & 7u) * 8u) = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
+    (void)hipGetLastError();
+    for (int64_t t = 0; t < p.num_tokens; t += kMaxTokensPerLaunch) {
+        GatherParams q = p;
+        q.num_tokens = p.num_tokens - t < kMaxTokensPerLaunch ? p.num_tokens - t : kMaxTokensPerLaunch;
+        q.slots = p.slots + t;
+        q.latent = p.latent + t * p.latent_stride;
+        q.rope = p.rope + t * p.rope_stride;
+        q.indexer = p.indexer + t * p.indexer_stride;
+        const uint32_t blocks = (uint32_t)((q.num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock);
+        gather_kernel<<<dim3(blocks), dim3(kGatherWaves * 64), 0, stream>>>(q, blocks);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kvpub

@@ -279,6 +279,36 @@ KVPUB_API kvpub_status kvpub_store(kvpub_ctx* ctx, uint32_t layer, int64_t num_t
     return map_hip(kvpub::launch_store(p, ctx->cfg.num_replicas, static_cast<hipStream_t>(stream)));
 }
 
+KVPUB_API kvpub_status kvpub_gather(kvpub_ctx* ctx, uint32_t replica, uint32_t layer, int64_t num_tokens,
+                                    const int64_t* slot_mapping, void* latent_out, int64_t latent_row_stride,
+                                    void* rope_out, int64_t rope_row_stride, void* indexer_out,
+                                    int64_t indexer_row_stride, kvpub_stream_t stream) {
+    if (!ctx || replica >= ctx->cfg.num_replicas) return KVPUB_ERR_INVALID_ARG;
+    // the outputs obey the same pointer, alignment and stride rules as the store's inputs
+    kvpub_status st = check_store(ctx, layer, num_tokens, latent_out, latent_row_stride, rope_out,
+                                  rope_row_stride, indexer_out, indexer_row_stride, slot_mapping);
+    if (st != KVPUB_OK || num_tokens == 0) return st;
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    kvpub::GatherParams g;
+    std::memset(&g, 0, sizeof g);
+    g.main_base = ctx->main_base[replica] + (uint64_t)layer * ctx->cfg.main_layer_stride;
+    g.idx_base = ctx->idx_base[replica] + (uint64_t)layer * ctx->cfg.idx_layer_stride;
+    g.main_page_stride = ctx->cfg.main_page_stride;
+    g.idx_page_stride = ctx->cfg.idx_page_stride;
+    g.capacity = (int64_t)(ctx->cfg.num_pages * KVPUB_SLOTS_PER_PAGE);
+    g.slots = slot_mapping;
+    g.num_tokens = num_tokens;
+    g.latent = static_cast<uint16_t*>(latent_out);
+    g.rope = static_cast<uint16_t*>(rope_out);
+    g.indexer = static_cast<uint16_t*>(indexer_out);
+    g.latent_stride = latent_row_stride;
+    g.rope_stride = rope_row_stride;
+    g.indexer_stride = indexer_row_stride;
+    g.invalid_count = reinterpret_cast<unsigned long long*>(ctx->words + kvpub::kInvalidOffset);
+    return map_hip(kvpub::launch_gather(g, static_cast<hipStream_t>(stream)));
+}
+
 KVPUB_API kvpub_status kvpub_fence(kvpub_ctx* ctx, uint32_t lane, kvpub_stream_t stream) {
     if (!ctx || lane >= ctx->cfg.num_lanes) return KVPUB_ERR_INVALID_ARG;
     DeviceGuard guard(ctx->cfg.device);

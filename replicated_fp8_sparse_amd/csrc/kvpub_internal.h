@@ -54,6 +54,25 @@ struct FenceParams {
 
 // Enqueue one store kernel on `stream`; returns the launch status.
 hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream);
+struct GatherParams {
+    const uint8_t* main_base;    // the replica, already offset to the layer
+    const uint8_t* idx_base;
+    uint64_t main_page_stride;   // bytes
+    uint64_t idx_page_stride;
+    int64_t capacity;            // num_pages * 64
+    const int64_t* slots;
+    int64_t num_tokens;
+    uint16_t* latent;            // bf16 outputs
+    uint16_t* rope;
+    uint16_t* indexer;
+    int64_t latent_stride;       // elements
+    int64_t rope_stride;
+    int64_t indexer_stride;
+    unsigned long long* invalid_count;
+};
+
+// Enqueue the dequantizing gather on `stream`; returns the launch status.
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 // Enqueue one fence kernel on `stream`.
 hipError_t launch_fence(const FenceParams& p, hipStream_t stream);
 

@@ -38,7 +38,7 @@ IDX_SCALES_OFFSET = 64 * 128
 MAX_REPLICAS = 8
 
 # Every function include/kvpub.h declares.
-EXPORTS = ("kvpub_config_init", "kvpub_create", "kvpub_store", "kvpub_fence",
+EXPORTS = ("kvpub_config_init", "kvpub_create", "kvpub_store", "kvpub_gather", "kvpub_fence",
            "kvpub_graph_create", "kvpub_graph_replay", "kvpub_graph_destroy",
            "kvpub_epoch_read", "kvpub_error_read", "kvpub_participant_signal",
            "kvpub_destroy", "kvpub_strerror", "kvpub_abi_version")
@@ -99,6 +99,7 @@ def load(path=LIB_PATH):
         "kvpub_config_init": (None, [cfgp, u32, u32, u64]),
         "kvpub_create": (i32, [cfgp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp)]),
         "kvpub_store": (i32, [vp, u32, i64, vp, i64, vp, i64, vp, i64, vp, vp]),
+        "kvpub_gather": (i32, [vp, u32, u32, i64, vp, vp, i64, vp, i64, vp, i64, vp]),
         "kvpub_fence": (i32, [vp, u32, vp]),
         "kvpub_graph_create": (i32, [vp, ctypes.POINTER(kvpub_layer_io), u32, u32, ctypes.POINTER(vp)]),
         "kvpub_graph_replay": (i32, [vp, vp]),
@@ -154,6 +155,13 @@ def kvpub_store(ctx, layer, num_tokens, latent, latent_row_stride, rope, rope_ro
     return load().kvpub_store(ctx, layer, num_tokens, latent, latent_row_stride, rope,
                               rope_row_stride, indexer, indexer_row_stride, slot_mapping,
                               stream)
+
+
+def kvpub_gather(ctx, replica, layer, num_tokens, slot_mapping, latent_out, latent_row_stride,
+                 rope_out, rope_row_stride, indexer_out, indexer_row_stride, stream=0):
+    return load().kvpub_gather(ctx, replica, layer, num_tokens, slot_mapping, latent_out,
+                               latent_row_stride, rope_out, rope_row_stride, indexer_out,
+                               indexer_row_stride, stream)
 
 
 def kvpub_fence(ctx, lane=0, stream=0):

@@ -60,6 +60,7 @@ def test_host_side_argument_checks():
     st, ctx = kvpub.kvpub_create(cfg, [16, 40], [16, 32])         # misaligned base
     assert st == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_store(None, 0, 4, 16, 512, 16, 64, 16, 128, 16, 0) == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_gather(None, 0, 0, 4, 16, 16, 512, 16, 64, 16, 128, 0) == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_fence(None, 0, 0) == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_graph_replay(None, 0) == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_graph_destroy(None) == kvpub.KVPUB_OK
