@@ -192,6 +192,8 @@ def main():
     kvpub.check(st)
     assert invalid == 0 and flags == 0
 
+    gather = None if args.no_extras else gather_line(torch, kvpub, ctx, slots, T, valid, stream)
+
     extras = {}
     decode = None
     if not args.no_extras:
@@ -243,6 +245,8 @@ def main():
         result["store_only"] = extras
     if decode:
         result["decode_store_fence"] = decode
+    if gather:
+        result["gather"] = gather
 
     kvpub.kvpub_graph_destroy(graph)
 
@@ -304,6 +308,40 @@ def store_only_extras(torch, kvpub, W, stream):
         del mb, ib, lat, rope, idx
         torch.cuda.empty_cache()
     return out
+
+
+GATHER_READ_BYTES_PER_TOKEN = 656 + 128 + 4          # one replica's Main-KV row + Indexer-K
+GATHER_WRITE_BYTES_PER_TOKEN = (512 + 64 + 128) * 2  # bf16 rows out
+
+
+def gather_line(torch, kvpub, ctx, slots, T, valid, stream):
+    """The reader side on the graph workload's layer: kvpub_gather of the T=4096
+    slots of layer 0 from replica 0 back to bf16 rows, warm (back-to-back launches
+    over the 61 layers) and cold (one launch after a 1 GiB scratch write)."""
+    sh = stream.cuda_stream
+    L = 61
+    lat = torch.empty((T, 512), dtype=torch.bfloat16, device="cuda")
+    rope = torch.empty((T, 64), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((T, 128), dtype=torch.bfloat16, device="cuda")
+
+    def launch(l):
+        return kvpub.kvpub_gather(ctx, 0, l % L, T, slots.data_ptr(), lat.data_ptr(), 512, rope.data_ptr(), 64,
+                                  idx.data_ptr(), 128, sh)
+
+    for l in range(L):
+        kvpub.check(launch(l))
+    n = 4 * L
+    with Timer(torch, stream) as tm:
+        for i in range(n):
+            launch(i)
+    us = tm.ms * 1e3 / n
+    cold = cold_launch_us(torch, stream, launch, L)
+    b = valid * (GATHER_READ_BYTES_PER_TOKEN + GATHER_WRITE_BYTES_PER_TOKEN)
+    return {"kernel": "gather_kernel", "tokens": T, "avg_launch_us": round(us, 3), "alg_bytes": b,
+            "gbps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tokens_per_s": round(valid / (us * 1e-6), 1), "cold_launch_us": round(cold, 3),
+            "how": "eager back-to-back launches over the 61 layer caches of replica 0 (warm), and single "
+                   "launches after a 1 GiB scratch write (cold); bytes = 788 B read + 1408 B written per token"}
 
 
 def cold_launch_us(torch, stream, launch, copies, n=12):
