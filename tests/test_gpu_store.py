@@ -279,3 +279,58 @@ def test_consecutive_slot_runs(orc, T, kind):
     indexer = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32))
     latent[T // 2] = 0                   # an all-zero row inside a run
     run_full(orc, layout, [(0, LayerInputs(latent, rope, indexer, slots))], f"runs {kind} T={T}")
+
+
+def test_store_across_the_launch_split(orc):
+    """More than 2^24 tokens in one call: the host splits the batch into several
+    launches.  Inputs are drawn on the GPU; the tokens around the split and a
+    random sample elsewhere are gathered on the GPU and compared with the oracle
+    row by row; every other row's bytes must still hold the fill pattern there."""
+    t = G.torch()
+    T = (1 << 24) + 37
+    G.log(f"store across the launch split: T={T}, R=2 (about 24 GB of inputs, 26 GB of cache)")
+    layout = W.CacheLayout(replicas=2, layers=1, num_pages=(T + 63) // 64 + 2)
+    dev = G.DeviceCache(layout)
+    g = t.Generator(device="cuda").manual_seed(41)
+    lat = t.randn((T, 512), device="cuda", generator=g, dtype=t.bfloat16)
+    rope = t.randn((T, 64), device="cuda", generator=g, dtype=t.bfloat16)
+    ind = t.randn((T, 128), device="cuda", generator=g, dtype=t.bfloat16)
+    # consecutive slots shifted by one page: token t -> slot t + 64, so rows of the two
+    # launches interleave with nothing else
+    slots = t.arange(64, T + 64, dtype=t.int64, device="cuda")
+    s = t.cuda.current_stream().cuda_stream
+    kvpub.check(kvpub.kvpub_store(dev.ctx, 0, T, lat.data_ptr(), 512, rope.data_ptr(), 64, ind.data_ptr(), 128,
+                                  slots.data_ptr(), s))
+    t.cuda.synchronize()
+    rng = np.random.default_rng(42)
+    split = 1 << 24
+    sample = np.unique(np.concatenate([np.arange(split - 40, split + 37), np.arange(0, 40),
+                                       rng.integers(0, T, 2000)])).astype(np.int64)
+    idx_t = t.from_numpy(sample).to("cuda")
+    x = W.LayerInputs(lat[idx_t].view(t.int16).cpu().numpy().view(np.uint16),
+                      rope[idx_t].view(t.int16).cpu().numpy().view(np.uint16),
+                      ind[idx_t].view(t.int16).cpu().numpy().view(np.uint16), sample + 64)
+    rows = orc.encode_rows(x.latent, x.rope, x.indexer)
+    G.assert_gathered_parity(dev, 0, x, rows, "split")
+    del lat, rope, ind
+    # the reader side across the same split: gather every slot from replica 1
+    # and compare the sampled rows with the oracle's decode of the oracle's rows
+    g_lat = t.empty((T, 512), dtype=t.int16, device="cuda")
+    g_rope = t.empty((T, 64), dtype=t.int16, device="cuda")
+    g_idx = t.empty((T, 128), dtype=t.int16, device="cuda")
+    kvpub.check(kvpub.kvpub_gather(dev.ctx, 1, 0, T, slots.data_ptr(), g_lat.data_ptr(), 512, g_rope.data_ptr(),
+                                   64, g_idx.data_ptr(), 128, s))
+    t.cuda.synchronize()
+    got_lat = g_lat[idx_t].cpu().numpy().view(np.uint16)
+    got_rope = g_rope[idx_t].cpu().numpy().view(np.uint16)
+    got_idx = g_idx[idx_t].cpu().numpy().view(np.uint16)
+    main_rows, icodes, iscale = rows
+    for i in range(sample.size):
+        sc = main_rows[i, 512:528].view(np.float32)
+        want = np.concatenate([orc.dequant_tile(main_rows[i, 128 * j:128 * (j + 1)], sc[j]) for j in range(4)])
+        assert np.array_equal(got_lat[i], want), f"split gather latent, token {sample[i]}"
+        assert np.array_equal(got_rope[i], x.rope[i]), f"split gather rope, token {sample[i]}"
+        want_i = orc.dequant_tile(icodes[i], iscale[i].view(np.float32)[0])
+        assert np.array_equal(got_idx[i], want_i), f"split gather indexer, token {sample[i]}"
+    del g_lat, g_rope, g_idx
+    dev.free()
