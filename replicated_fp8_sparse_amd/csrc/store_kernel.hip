@@ -49,9 +49,6 @@ typedef __attribute__((address_space(3))) uint8_t lbyte;   // a byte in LDS
 template <class T> using gptr = __attribute__((address_space(1))) T*;
 template <class T> using lptr = __attribute__((address_space(3))) T*;
 
-#ifndef KVPUB_ROW_RUN
-#define KVPUB_ROW_RUN 1   // assemble runs of 4 consecutive rows in LDS and store them whole
-#endif
 constexpr uint32_t kRunBytes = 4 * 656;   // 2624 = 164 x 16 B
 constexpr int64_t kCacheBytesPerToken = 656 + 128 + 4;              // per replica
 constexpr int64_t kStreamingStoreBytes = int64_t(16) << 20;         // launches writing at most this stream
@@ -250,7 +247,8 @@ __device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2,
     for (int k = 0; k < 4; ++k) d.row[k] = row[k];
     tok = __builtin_amdgcn_readfirstlane(tok);   // uniform; computed once, before the wait
     asm volatile("" : "+s"(tok));
-    uint32_t run = (KVPUB_ROW_RUN && tok == 0xFu && s1 == s0 + 1 && s2 == s0 + 2 && s3 == s0 + 3 && (s0 & 63) <= 60)
+    // the 4 rows are one contiguous run: all stored, consecutive slots of one page
+    uint32_t run = (tok == 0xFu && s1 == s0 + 1 && s2 == s0 + 2 && s3 == s0 + 3 && (s0 & 63) <= 60)
                        ? 1u : 0u;
     run = __builtin_amdgcn_readfirstlane(run);
     asm volatile("" : "+s"(run));
