@@ -72,47 +72,57 @@ __device__ __forceinline__ uint64_t pick4(uint64_t v0, uint64_t v1, uint64_t v2,
     return (i & 2u) ? b : a;
 }
 
-__global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(const GatherParams p, uint32_t num_blocks) {
+template <class T>
+__device__ __forceinline__ T ld_nt(const uint8_t* p) {
+    return __builtin_nontemporal_load((cgptr<T>)p);
+}
+
+// The arguments the first instructions need are plain scalars, preloaded in
+// SGPRs (kernel-argument preloading): the slot loads issue at once.
+__global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
+    const int64_t* __restrict__ slots, uint32_t num_tokens, const uint8_t* main_base, const uint8_t* idx_base,
+    uint64_t main_page_stride, uint64_t idx_page_stride, uint64_t capacity, const GatherParams p) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t t0 = ((int64_t)xcd_chunk(blockIdx.x, num_blocks) * kGatherWaves + wave) * 4;
-    if (t0 >= p.num_tokens) return;
-    const int64_t last = p.num_tokens - 1;
-    int64_t s[4];
+    const uint32_t num_blocks = (num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock;   // == gridDim.x
+    const uint32_t t0 = (xcd_chunk(blockIdx.x, num_blocks) * kGatherWaves + wave) * 4u;
+    if (t0 >= num_tokens) return;
+    const uint32_t last = num_tokens - 1;
     uint64_t row[4], irow[4], iscl[4];
     uint32_t ok = 0, nbad = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int64_t t = t0 + k < last ? t0 + k : last;
-        const int64_t v = t0 + k <= last ? p.slots[t] : -1;
-        const bool good = slot_ok(v, p.capacity);
+        const uint32_t t = t0 + k < last ? t0 + k : last;
+        const int64_t v = t0 + k <= last ? slots[t] : -1;
+        const bool good = slot_ok(v, (int64_t)capacity);
         nbad += (v != -1 && !good) ? 1u : 0u;
         ok |= good ? (1u << k) : 0u;
-        s[k] = good ? v : 0;                     // bad slots read slot 0 (in bounds) and emit zeros
-        const uint64_t page = (uint64_t)s[k] >> 6, in = (uint64_t)s[k] & 63u;
-        row[k] = page * p.main_page_stride + in * 656u;
-        irow[k] = page * p.idx_page_stride + in * 128u;
-        iscl[k] = page * p.idx_page_stride + 8192u + in * 4u;
+        const uint64_t s = good ? (uint64_t)v : 0u;   // bad slots read slot 0 (in bounds) and emit zeros
+        const uint64_t page = s >> 6, in = s & 63u;
+        row[k] = page * main_page_stride + in * 656u;
+        irow[k] = page * idx_page_stride + in * 128u;
+        iscl[k] = page * idx_page_stride + 8192u + in * 4u;
     }
-    if (nbad != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
     ok = __builtin_amdgcn_readfirstlane(ok);
 
-    // loads: four latent tiles (codes + the row's scale), the indexer tile, RoPE
+    // loads (read once: non-temporal): four latent tiles (codes + the row's
+    // scale), the indexer tile, RoPE
     const uint32_t j = lane >> 4, g = lane >> 4, r = (lane >> 3) & 3u;
     u32x2 code[5];
     float scale[5];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint8_t* rw = p.main_base + row[k];
-        code[k] = *(cgptr<u32x2>)(rw + lane * 8u);
-        scale[k] = *(cgptr<float>)(rw + 512u + j * 4u);
+        const uint8_t* rw = main_base + row[k];
+        code[k] = ld_nt<u32x2>(rw + lane * 8u);
+        scale[k] = ld_nt<float>(rw + 512u + j * 4u);
     }
     const uint64_t my_irow = pick4(irow[0], irow[1], irow[2], irow[3], g);
     const uint64_t my_iscl = pick4(iscl[0], iscl[1], iscl[2], iscl[3], g);
-    code[4] = *(cgptr<u32x2>)(p.idx_base + my_irow + (lane & 15u) * 8u);
-    scale[4] = *(cgptr<float>)(p.idx_base + my_iscl);
+    code[4] = ld_nt<u32x2>(idx_base + my_irow + (lane & 15u) * 8u);
+    scale[4] = ld_nt<float>(idx_base + my_iscl);
     const uint64_t my_rope = pick4(row[0], row[1], row[2], row[3], r) + 528u + (lane & 7u) * 16u;
-    const u32x4 rp = *(cgptr<u32x4>)(p.main_base + my_rope);
+    const u32x4 rp = ld_nt<u32x4>(main_base + my_rope);
+    if (nbad != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
 
     // dequantize and store
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -120,15 +130,15 @@ __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(const GatherP
     for (int k = 0; k < 4; ++k) {
         if (t0 + k > last) break;                // uniform: the tail of the last group
         const u32x4 v = ((ok >> k) & 1u) ? dequant8(code[k], scale[k]) : zero;
-        *(gptr<u32x4>)(p.latent + (t0 + k) * p.latent_stride + lane * 8u) = v;
+        *(gptr<u32x4>)(p.latent + (uint64_t)(t0 + k) * p.latent_stride + lane * 8u) = v;
     }
     if (t0 + g <= last) {
         const u32x4 v = ((ok >> g) & 1u) ? dequant8(code[4], scale[4]) : zero;
-        *(gptr<u32x4>)(p.indexer + (t0 + g) * p.indexer_stride + (lane & 15u) * 8u) = v;
+        *(gptr<u32x4>)(p.indexer + (uint64_t)(t0 + g) * p.indexer_stride + (lane & 15u) * 8u) = v;
     }
     if (lane < 32u && t0 + r <= last) {
         const u32x4 v = ((ok >> r) & 1u) ? rp : zero;
-        *(gptr<u32x4>)(p.rope + (t0 + r) * p.rope_stride + (lane & 7u) * 8u) = v;
+        *(gptr<u32x4>)(p.rope + (uint64_t)(t0 + r) * p.rope_stride + (lane & 7u) * 8u) = v;
     }
 }
 
@@ -144,7 +154,9 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
         q.rope = p.rope + t * p.rope_stride;
         q.indexer = p.indexer + t * p.indexer_stride;
         const uint32_t blocks = (uint32_t)((q.num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock);
-        gather_kernel<<<dim3(blocks), dim3(kGatherWaves * 64), 0, stream>>>(q, blocks);
+        gather_kernel<<<dim3(blocks), dim3(kGatherWaves * 64), 0, stream>>>(
+            q.slots, (uint32_t)q.num_tokens, q.main_base, q.idx_base, q.main_page_stride, q.idx_page_stride,
+            (uint64_t)q.capacity, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
