@@ -31,6 +31,10 @@
  *     that keep reading the local replica consume (PR #52863 Summary and
  *     Design: the existing attention kernels read the local replica in the
  *     fp8_ds_mla layout this path writes).
+ *   - kvpub_vmm_*: replica storage at stable virtual addresses that can grow
+ *     without moving (PR #52863 Relationship to existing work: the path builds
+ *     on a KV cache kept at a stable VA with its own rendezvous, so that the
+ *     cache can expand without re-exchanging views).
  *   - all-or-nothing creation and fail-closed fences (PR #54030 commit list:
  *     opt-in allocation is all-or-nothing at startup; a fence timeout must not
  *     let work continue).
@@ -90,6 +94,7 @@ extern "C" {
 
 typedef struct kvpub_ctx kvpub_ctx;
 typedef struct kvpub_graph kvpub_graph;
+typedef struct kvpub_vmm kvpub_vmm;
 typedef void *kvpub_stream_t; /* hipStream_t; NULL = the null stream */
 
 typedef enum {
@@ -183,6 +188,45 @@ KVPUB_API kvpub_status kvpub_gather(kvpub_ctx *ctx, uint32_t replica, uint32_t l
                                     const int64_t *slot_mapping, void *latent_out, int64_t latent_row_stride,
                                     void *rope_out, int64_t rope_row_stride, void *indexer_out,
                                     int64_t indexer_row_stride, kvpub_stream_t stream);
+
+/* Replica storage at stable virtual addresses, on cfg->device (vLLM PR
+ * #52863, Relationship to existing work: the replicated cache builds on a
+ * cache kept at a stable virtual address so that it can grow in place).
+ * Reserves address space for cfg->num_replicas replicas of cfg->num_layers
+ * layers of up to max_pages pages each (one Main-KV and one Indexer-K range
+ * per replica) and backs the first cfg->num_pages pages of every layer with
+ * device memory (contents undefined until written).  On success the layer
+ * strides in *cfg are set to the reserved per-layer spans (max_pages * page
+ * stride rounded up to the allocation granularity, plus one granule; every
+ * layer is a reservation of its own), main_bases[r] /
+ * idx_bases[r] receive the replicas' base addresses, and *cfg is ready for
+ * kvpub_create.  The bases never change for the object's lifetime.
+ * All-or-nothing: on failure nothing stays reserved or mapped and *out is
+ * NULL.  Only backed pages may be accessed: a context over this storage must
+ * not claim more pages than are backed (kvpub_vmm_grow keeps them equal). */
+KVPUB_API kvpub_status kvpub_vmm_create(kvpub_config *cfg, uint64_t max_pages, void **main_bases,
+                                        void **idx_bases, kvpub_vmm **out);
+
+/* Back every layer of every replica up to num_pages pages (num_pages <=
+ * max_pages; never shrinks).  Bytes already written and all addresses are
+ * unchanged.  If ctx is not NULL it must be a context over exactly this
+ * storage (same bases and strides, else KVPUB_ERR_INVALID_ARG); its capacity
+ * becomes the backed page count for launches made after the call (a graph
+ * captured before keeps the capacity it was captured with).  Host-side, not
+ * for use during stream capture or concurrently with launches on ctx from
+ * another thread.  On failure the page count stays as it was, except in the
+ * unlikely case that a layer's old backing could not be restored either:
+ * then the storage reports 0 pages, ctx (if given) accepts no slot any more,
+ * and KVPUB_ERR_HIP is returned.  Growing copies each layer's backed bytes
+ * once (the addresses stay, the physical memory behind them is replaced). */
+KVPUB_API kvpub_status kvpub_vmm_grow(kvpub_vmm *vmm, uint64_t num_pages, kvpub_ctx *ctx);
+
+/* Pages per layer currently backed. */
+KVPUB_API kvpub_status kvpub_vmm_pages(kvpub_vmm *vmm, uint64_t *num_pages);
+
+/* Synchronize the device, then unmap and release everything.  Contexts over
+ * this storage must be destroyed first. */
+KVPUB_API kvpub_status kvpub_vmm_destroy(kvpub_vmm *vmm);
 
 /* One fence on `lane`, asynchronously on `stream`: a single one-wavefront
  * kernel that adds 1 to the lane's device epoch with a system-scope release,

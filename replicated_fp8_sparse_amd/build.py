@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvpub.so")
-SOURCES = ["kvpub_api.hip", "store_kernel.hip", "fence_kernel.hip", "gather_kernel.hip"]
+SOURCES = ["kvpub_api.hip", "store_kernel.hip", "fence_kernel.hip", "gather_kernel.hip", "vmm.hip"]
 ARCH = "gfx950"
 
 # No fast-math, no FP contraction (explicit fmaf only); packed-fp32 instructions

@@ -178,6 +178,25 @@ kvpub_status sync_device() {
 
 }  // namespace
 
+namespace kvpub {
+
+bool ctx_uses_storage(const kvpub_ctx* ctx, uint32_t replicas, uint8_t* const* main_bases,
+                      uint8_t* const* idx_bases, uint64_t main_layer_stride, uint64_t idx_layer_stride,
+                      uint64_t main_page_stride, uint64_t idx_page_stride) {
+    if (ctx->cfg.num_replicas != replicas) return false;
+    if (ctx->cfg.main_layer_stride != main_layer_stride || ctx->cfg.idx_layer_stride != idx_layer_stride)
+        return false;
+    if (ctx->cfg.main_page_stride != main_page_stride || ctx->cfg.idx_page_stride != idx_page_stride)
+        return false;
+    for (uint32_t r = 0; r < replicas; ++r)
+        if (ctx->main_base[r] != main_bases[r] || ctx->idx_base[r] != idx_bases[r]) return false;
+    return true;
+}
+
+void ctx_set_pages(kvpub_ctx* ctx, uint64_t num_pages) { ctx->cfg.num_pages = num_pages; }
+
+}  // namespace kvpub
+
 extern "C" {
 
 KVPUB_API void kvpub_config_init(kvpub_config* cfg, uint32_t num_replicas, uint32_t num_layers,

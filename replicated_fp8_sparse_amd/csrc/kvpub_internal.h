@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct kvpub_ctx;
+
 namespace kvpub {
 
 constexpr int kMaxReplicas = 8;
@@ -73,6 +75,12 @@ struct GatherParams {
 
 // Enqueue the dequantizing gather on `stream`; returns the launch status.
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+// True if ctx's replicas are exactly these bases with these layer and page strides.
+bool ctx_uses_storage(const kvpub_ctx* ctx, uint32_t replicas, uint8_t* const* main_bases,
+                      uint8_t* const* idx_bases, uint64_t main_layer_stride, uint64_t idx_layer_stride,
+                      uint64_t main_page_stride, uint64_t idx_page_stride);
+// Raise (or set) the number of pages per layer that ctx's launches may write.
+void ctx_set_pages(kvpub_ctx* ctx, uint64_t num_pages);
 // Enqueue one fence kernel on `stream`.
 hipError_t launch_fence(const FenceParams& p, hipStream_t stream);
 

@@ -41,7 +41,8 @@ MAX_REPLICAS = 8
 EXPORTS = ("kvpub_config_init", "kvpub_create", "kvpub_store", "kvpub_gather", "kvpub_fence",
            "kvpub_graph_create", "kvpub_graph_replay", "kvpub_graph_destroy",
            "kvpub_epoch_read", "kvpub_error_read", "kvpub_participant_signal",
-           "kvpub_destroy", "kvpub_strerror", "kvpub_abi_version")
+           "kvpub_destroy", "kvpub_strerror", "kvpub_abi_version", "kvpub_vmm_create",
+           "kvpub_vmm_grow", "kvpub_vmm_pages", "kvpub_vmm_destroy")
 
 
 class kvpub_config(ctypes.Structure):
@@ -110,6 +111,10 @@ def load(path=LIB_PATH):
         "kvpub_destroy": (i32, [vp]),
         "kvpub_strerror": (ctypes.c_char_p, [i32]),
         "kvpub_abi_version": (u32, []),
+        "kvpub_vmm_create": (i32, [cfgp, u64, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp)]),
+        "kvpub_vmm_grow": (i32, [vp, u64, vp]),
+        "kvpub_vmm_pages": (i32, [vp, ctypes.POINTER(u64)]),
+        "kvpub_vmm_destroy": (i32, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -212,6 +217,33 @@ def kvpub_destroy(ctx):
 
 def kvpub_abi_version():
     return load().kvpub_abi_version()
+
+
+def kvpub_vmm_create(cfg, max_pages):
+    """Returns (status, vmm handle or None, main base addresses, idx base addresses);
+    cfg's layer strides are updated in place."""
+    R = cfg.num_replicas
+    mb = (ctypes.c_void_p * max(R, 1))()
+    ib = (ctypes.c_void_p * max(R, 1))()
+    out = ctypes.c_void_p()
+    st = load().kvpub_vmm_create(ctypes.byref(cfg), max_pages, mb, ib, ctypes.byref(out))
+    if st != KVPUB_OK:
+        return st, None, [], []
+    return st, out.value, [mb[r] for r in range(R)], [ib[r] for r in range(R)]
+
+
+def kvpub_vmm_grow(vmm, num_pages, ctx=None):
+    return load().kvpub_vmm_grow(vmm, num_pages, ctx)
+
+
+def kvpub_vmm_pages(vmm):
+    v = ctypes.c_uint64()
+    st = load().kvpub_vmm_pages(vmm, ctypes.byref(v))
+    return st, v.value
+
+
+def kvpub_vmm_destroy(vmm):
+    return load().kvpub_vmm_destroy(vmm)
 
 
 def kvpub_strerror(status):

@@ -240,3 +240,27 @@ def assert_replicas_identical(dev: DeviceCache):
     for r in range(1, dev.layout.replicas):
         assert t.equal(dev.main[r], dev.main[0]), f"main replica {r} differs from replica 0"
         assert t.equal(dev.idx[r], dev.idx[0]), f"indexer replica {r} differs from replica 0"
+
+
+def hip_runtime():
+    """The HIP runtime library already loaded in this process (the one torch and
+    libkvpub share), for raw-address copies and fills in tests."""
+    import ctypes
+    path = None
+    with open("/proc/self/maps") as fh:
+        for line in fh:
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+    assert path, "HIP runtime not loaded"
+    lib = ctypes.CDLL(path)
+    lib.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    lib.hipMemcpy.restype = ctypes.c_int
+    lib.hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
+    lib.hipMemset.restype = ctypes.c_int
+    lib.hipDeviceSynchronize.restype = ctypes.c_int
+    return lib
+
+
+HIP_MEMCPY_HOST_TO_DEVICE = 1
+HIP_MEMCPY_DEVICE_TO_HOST = 2

@@ -67,6 +67,17 @@ def test_host_side_argument_checks():
     assert kvpub.kvpub_destroy(None) == kvpub.KVPUB_OK
     st, _ = kvpub.kvpub_epoch_read(None, 0)
     assert st == kvpub.KVPUB_ERR_INVALID_ARG
+    # VMM storage: argument checks come before any HIP call
+    cfg = kvpub.kvpub_config_init(2, 1, 4)
+    assert kvpub.kvpub_vmm_create(cfg, 3)[0] == kvpub.KVPUB_ERR_INVALID_ARG       # max below the initial pages
+    cfg.num_replicas = 0
+    assert kvpub.kvpub_vmm_create(cfg, 8)[0] == kvpub.KVPUB_ERR_INVALID_ARG
+    cfg = kvpub.kvpub_config_init(2, 1, 4)
+    cfg.idx_page_stride = 8 * 1024                                                # below one Indexer-K page
+    assert kvpub.kvpub_vmm_create(cfg, 8)[0] == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_vmm_grow(None, 8) == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_vmm_pages(None)[0] == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_vmm_destroy(None) == kvpub.KVPUB_OK
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -1,0 +1,146 @@
+"""Replica storage at stable virtual addresses (kvpub_vmm_*): stores and gathers
+into VMM-backed replicas are byte-exact against the oracle, growing the storage
+keeps every written byte and every address, and the grown capacity becomes
+usable.  Only backed ranges are ever touched by the test (slots beyond the
+context's capacity are skipped and counted by the kernels)."""
+import numpy as np
+import pytest
+
+from replicated_fp8_sparse_amd import kvpub, workloads as W
+import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+MAIN_PAGE, IDX_PAGE = 64 * 656, 64 * 132
+
+
+def _ptr(a):
+    return a.ctypes.data
+
+
+class Mirror:
+    """Host replicas with the VMM layout, initialised like the device's backed pages."""
+
+    def __init__(self, cfg, layers):
+        self.cfg, self.L = cfg, layers
+        self.main = [np.full(layers * cfg.main_layer_stride, W.FILL, np.uint8) for _ in range(cfg.num_replicas)]
+        self.idx = [np.full(layers * cfg.idx_layer_stride, W.FILL, np.uint8) for _ in range(cfg.num_replicas)]
+
+    def store(self, orc, pages, layer, x):
+        c = self.cfg
+        return orc.store(self.main, self.idx, num_pages=pages, main_page_stride=c.main_page_stride,
+                         main_layer_stride=c.main_layer_stride, idx_page_stride=c.idx_page_stride,
+                         idx_layer_stride=c.idx_layer_stride, layer=layer, latent=x.latent, rope=x.rope,
+                         indexer=x.indexer, slot_mapping=x.slots)
+
+
+def fill_pages(hip, cfg, mb, ib, p0, p1, layers):
+    for r in range(cfg.num_replicas):
+        for l in range(layers):
+            assert hip.hipMemset(mb[r] + l * cfg.main_layer_stride + p0 * MAIN_PAGE, W.FILL, (p1 - p0) * MAIN_PAGE) == 0
+            assert hip.hipMemset(ib[r] + l * cfg.idx_layer_stride + p0 * IDX_PAGE, W.FILL, (p1 - p0) * IDX_PAGE) == 0
+    assert hip.hipDeviceSynchronize() == 0
+
+
+def compare_backed(hip, cfg, mb, ib, mirror, pages, layers, what):
+    for r in range(cfg.num_replicas):
+        for l in range(layers):
+            for base, stride, page, host in ((mb[r], cfg.main_layer_stride, MAIN_PAGE, mirror.main[r]),
+                                             (ib[r], cfg.idx_layer_stride, IDX_PAGE, mirror.idx[r])):
+                n = pages * page
+                got = np.empty(n, np.uint8)
+                assert hip.hipMemcpy(_ptr(got), base + l * stride, n, G.HIP_MEMCPY_DEVICE_TO_HOST) == 0
+                want = host[l * stride:l * stride + n]
+                bad = np.nonzero(got != want)[0]
+                assert bad.size == 0, f"{what}: replica {r} layer {l}: {bad.size} bytes differ, first at {bad[0]}"
+
+
+def test_vmm_store_grow_gather(orc):
+    G.log("vmm: R=2, L=3, 40 pages backed of 1000 reserved, grow to 300")
+    t = G.torch()
+    hip = G.hip_runtime()
+    R, L, P0, PMAX, P1 = 2, 3, 40, 1000, 300
+    cfg = kvpub.kvpub_config_init(R, L, P0)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, PMAX)
+    kvpub.check(st, "kvpub_vmm_create")
+    try:
+        assert cfg.main_layer_stride >= PMAX * MAIN_PAGE and cfg.idx_layer_stride >= PMAX * IDX_PAGE
+        assert all(b % 16 == 0 for b in mb + ib)
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, P0)
+        fill_pages(hip, cfg, mb, ib, 0, P0, L)
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st, "kvpub_create")
+        mirror = Mirror(cfg, L)
+        rng = np.random.default_rng(51)
+        s = t.cuda.current_stream().cuda_stream
+
+        def store(layer, slots):
+            x = W.LayerInputs(*W._normal_rows(rng, slots.size), slots.astype(np.int64))
+            d = G.DeviceInputs(x)
+            kvpub.check(kvpub.kvpub_store(ctx, layer, d.T, d.latent.data_ptr(), 512, d.rope.data_ptr(), 64,
+                                          d.indexer.data_ptr(), 128, d.slots.data_ptr(), s))
+            t.cuda.synchronize()
+            return x
+
+        # before growing: slots in the backed pages, plus pads and slots beyond the capacity
+        slots = rng.permutation(P0 * 64)[:1500]
+        slots = np.concatenate([slots, [-1, -1, P0 * 64, PMAX * 64 - 1, P1 * 64]])
+        x1 = store(1, slots)
+        assert mirror.store(orc, P0, 1, x1) == 3
+        st, invalid, _ = kvpub.kvpub_error_read(ctx, True)
+        assert invalid == 3
+        compare_backed(hip, cfg, mb, ib, mirror, P0, L, "before growing")
+
+        # grow: same bases, more pages; the context's capacity follows
+        kvpub.check(kvpub.kvpub_vmm_grow(vmm, P1, ctx), "kvpub_vmm_grow")
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, P1)
+        fill_pages(hip, cfg, mb, ib, P0, P1, L)
+        compare_backed(hip, cfg, mb, ib, mirror, P0, L, "after growing, old pages")
+        slots = np.concatenate([rng.permutation(np.arange(P0 * 64, P1 * 64))[:3000], [P1 * 64, -1]])
+        x2 = store(2, slots)
+        slots = rng.permutation(np.setdiff1d(np.arange(P1 * 64), x1.slots))[:2000]
+        x3 = store(1, slots)
+        assert mirror.store(orc, P1, 2, x2) == 1
+        assert mirror.store(orc, P1, 1, x3) == 0
+        compare_backed(hip, cfg, mb, ib, mirror, P1, L, "after growing")
+
+        # the reader side over old and new pages
+        want_slots = np.concatenate([x1.slots[:200], x2.slots[:200], x3.slots[:200]]).astype(np.int64)
+        T = want_slots.size
+        outs = [t.zeros((T, w), dtype=t.int16, device="cuda") for w in (512, 64, 128)]
+        sd = G.to_dev_i64(want_slots)
+        for layer in (1, 2):
+            kvpub.check(kvpub.kvpub_gather(ctx, 1, layer, T, sd.data_ptr(), outs[0].data_ptr(), 512,
+                                           outs[1].data_ptr(), 64, outs[2].data_ptr(), 128, s))
+            t.cuda.synchronize()
+            c = cfg
+            want = orc.gather(mirror.main[1], mirror.idx[1], num_pages=P1, main_page_stride=c.main_page_stride,
+                              main_layer_stride=c.main_layer_stride, idx_page_stride=c.idx_page_stride,
+                              idx_layer_stride=c.idx_layer_stride, layer=layer, slot_mapping=want_slots)
+            for got, w, name in zip(outs, want[:3], ("latent", "rope", "indexer")):
+                assert np.array_equal(got.cpu().numpy().view(np.uint16), w), f"vmm gather {name} layer {layer}"
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm), "kvpub_vmm_destroy")
+
+
+def test_vmm_bad_arguments():
+    bad = kvpub.KVPUB_ERR_INVALID_ARG
+    cfg = kvpub.kvpub_config_init(1, 2, 8)
+    st, vmm, _, _ = kvpub.kvpub_vmm_create(cfg, 4)                # max below the initial pages
+    assert st == bad and vmm is None
+    cfg = kvpub.kvpub_config_init(9, 2, 8)                        # too many replicas
+    assert kvpub.kvpub_vmm_create(cfg, 16)[0] == bad
+    cfg = kvpub.kvpub_config_init(1, 2, 8)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, 16)
+    kvpub.check(st)
+    try:
+        assert kvpub.kvpub_vmm_grow(vmm, 17) == bad                # beyond the reservation
+        other = G.DeviceCache(W.CacheLayout(replicas=1, layers=2, num_pages=8))
+        assert kvpub.kvpub_vmm_grow(vmm, 12, other.ctx) == bad     # a context over other storage
+        other.free()
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, 8)
+        assert kvpub.kvpub_vmm_grow(vmm, 4) == kvpub.KVPUB_OK      # never shrinks
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, 8)
+    finally:
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
