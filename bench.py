@@ -195,10 +195,11 @@ def main():
     gather = None if args.no_extras else gather_line(torch, kvpub, ctx, slots, T, valid, stream)
 
     extras = {}
-    decode = None
+    decode = fanout = None
     if not args.no_extras:
         extras = store_only_extras(torch, kvpub, W, stream)
         decode = decode_eager(torch, kvpub, W, stream)
+        fanout = fanout_ab(torch, kvpub, W, stream)
 
     result = {
         "metric": "cache-store tokens/sec and achieved HBM GB/s (% of peak); fence µs/layer",
@@ -247,6 +248,8 @@ def main():
         result["decode_store_fence"] = decode
     if gather:
         result["gather"] = gather
+    if fanout:
+        result["fanout_ab"] = fanout
 
     kvpub.kvpub_graph_destroy(graph)
 
@@ -259,21 +262,32 @@ def main():
 
 def store_only_extras(torch, kvpub, W, stream):
     """Store-kernel bandwidth on the prefill (T=8192, R=4) and heavy-tail (T=32768, R=4)
-    workloads: eager back-to-back launches over rotated input copies, HIP events."""
+    workloads: eager back-to-back launches over rotated input copies, HIP events.  The
+    heavy shape is run twice: on ordinary device allocations and on VMM-backed replicas
+    (kvpub_vmm_create), whose mappings the kernel reaches through the same pointers."""
     out = {}
     sh = stream.cuda_stream
-    for name, fn, copies in (("prefill_T8192_R4", W.prefill, 8), ("heavy_T32768_R4", W.heavy, 8)):
+    for name, fn, copies, vmm in (("prefill_T8192_R4", W.prefill, 8, False), ("heavy_T32768_R4", W.heavy, 8, False),
+                                  ("heavy_T32768_R4_vmm", W.heavy, 8, True)):
         layout, x = fn()
         print(f"[bench] store-only {name}", file=sys.stderr, flush=True)
         R = layout.replicas
-        mb = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
-        ib = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
-        for b in mb:
-            layout.fill_device(b, "main")
-        for b in ib:
-            layout.fill_device(b, "idx")
         cfg = kvpub.kvpub_config_init(R, 1, layout.num_pages)
-        st, ctx = kvpub.kvpub_create(cfg, [b.data_ptr() for b in mb], [b.data_ptr() for b in ib])
+        storage = None
+        if vmm:
+            # the store never reads the cache, so the VMM pages need no fill for timing
+            st, storage, mbp, ibp = kvpub.kvpub_vmm_create(cfg, layout.num_pages)
+            kvpub.check(st, "kvpub_vmm_create")
+            mb = ib = None
+        else:
+            mb = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+            ib = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+            for b in mb:
+                layout.fill_device(b, "main")
+            for b in ib:
+                layout.fill_device(b, "idx")
+            mbp, ibp = [b.data_ptr() for b in mb], [b.data_ptr() for b in ib]
+        st, ctx = kvpub.kvpub_create(cfg, mbp, ibp)
         kvpub.check(st)
         T = x.slots.size
         lat = torch.from_numpy(x.latent.view(np.int16)).to("cuda").repeat(copies, 1, 1)
@@ -301,12 +315,78 @@ def store_only_extras(torch, kvpub, W, stream):
                      "tokens_per_s": round(valid / (us * 1e-6), 1),
                      "cold_launch_us": round(cold, 3),
                      "cold_frac": round(b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "storage": "vmm" if vmm else "device allocations",
                      "how": "warm: back-to-back launches over rotated input copies; cold: each launch "
                             "timed alone after writing a 1 GiB scratch buffer (flushes L2 and the "
                             "256 MB memory-side cache)"}
         kvpub.check(kvpub.kvpub_destroy(ctx))
+        if storage is not None:
+            kvpub.check(kvpub.kvpub_vmm_destroy(storage), "kvpub_vmm_destroy")
         del mb, ib, lat, rope, idx
         torch.cuda.empty_cache()
+    return out
+
+
+def fanout_ab(torch, kvpub, W, stream):
+    """The pages' A/B of the fan-out, on one GPU: one launch that reads each token's
+    bf16 rows once and writes all R replicas, against R launches of single-replica
+    contexts over the same buffers, each re-reading the rows (an insert per replica).
+    Both write identical bytes; each is timed as replays of a captured graph over
+    rotated input copies."""
+    out = {}
+    sh = stream.cuda_stream
+    for name, fn in (("prefill_T8192_R4", W.prefill), ("heavy_T32768_R4", W.heavy)):
+        layout, x = fn()
+        print(f"[bench] fan-out A/B {name}", file=sys.stderr, flush=True)
+        R, copies = layout.replicas, 4
+        mb = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        ib = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        cfg = kvpub.kvpub_config_init(R, 1, layout.num_pages)
+        st, fused = kvpub.kvpub_create(cfg, [b.data_ptr() for b in mb], [b.data_ptr() for b in ib])
+        kvpub.check(st)
+        single = []
+        for r in range(R):
+            c1 = kvpub.kvpub_config_init(1, 1, layout.num_pages)
+            st, c = kvpub.kvpub_create(c1, [mb[r].data_ptr()], [ib[r].data_ptr()])
+            kvpub.check(st)
+            single.append(c)
+        T = x.slots.size
+        lat = torch.from_numpy(x.latent.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+        rope = torch.from_numpy(x.rope.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+        idx = torch.from_numpy(x.indexer.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+        slots = torch.from_numpy(x.slots).to("cuda")
+        valid = int(((x.slots >= 0) & (x.slots < layout.capacity)).sum())
+
+        def store(ctx, c):
+            kvpub.check(kvpub.kvpub_store(ctx, 0, T, lat[c].data_ptr(), 512, rope[c].data_ptr(), 64,
+                                          idx[c].data_ptr(), 128, slots.data_ptr(), sh))
+
+        def timed(body):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for c in range(copies):
+                        body(c)
+                g.replay()
+                reps = 8
+                with Timer(torch, stream) as tm:
+                    for _ in range(reps):
+                        g.replay()
+            return tm.ms * 1e3 / (reps * copies)
+
+        fused_us = timed(lambda c: store(fused, c))
+        split_us = timed(lambda c: [store(single[r], c) for r in range(R)])
+        out[name] = {"fused_us": round(fused_us, 3), "per_replica_launches_us": round(split_us, 3),
+                     "speedup": round(split_us / fused_us, 3), "fused_bytes": alg_bytes(valid, R),
+                     "per_replica_bytes": R * alg_bytes(valid, 1)}
+        for c in single:
+            kvpub.check(kvpub.kvpub_destroy(c))
+        kvpub.check(kvpub.kvpub_destroy(fused))
+        del mb, ib, lat, rope, idx
+        torch.cuda.empty_cache()
+    out["how"] = ("one store launch writing all R replicas vs R single-replica store launches each re-reading "
+                  "the bf16 rows, both captured in a graph over 4 rotated input copies and replayed; "
+                  "microseconds per batch")
     return out
 
 
@@ -316,8 +396,9 @@ GATHER_WRITE_BYTES_PER_TOKEN = (512 + 64 + 128) * 2  # bf16 rows out
 
 def gather_line(torch, kvpub, ctx, slots, T, valid, stream):
     """The reader side on the graph workload's layer: kvpub_gather of the T=4096
-    slots of layer 0 from replica 0 back to bf16 rows, warm (back-to-back launches
-    over the 61 layers) and cold (one launch after a 1 GiB scratch write)."""
+    slots from replica 0 back to bf16 rows, over the 61 layers.  Timed as replays of
+    a graph of the 61 gathers (as the store is), eagerly back to back (host launch
+    cost included), and cold (one launch after a 1 GiB scratch write)."""
     sh = stream.cuda_stream
     L = 61
     lat = torch.empty((T, 512), dtype=torch.bfloat16, device="cuda")
@@ -334,14 +415,28 @@ def gather_line(torch, kvpub, ctx, slots, T, valid, stream):
     with Timer(torch, stream) as tm:
         for i in range(n):
             launch(i)
-    us = tm.ms * 1e3 / n
+    eager_us = tm.ms * 1e3 / n
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for l in range(L):
+                kvpub.check(launch(l))
+        for _ in range(2):
+            g.replay()
+        reps = 8
+        with Timer(torch, stream) as tg:
+            for _ in range(reps):
+                g.replay()
+    us = tg.ms * 1e3 / (reps * L)
     cold = cold_launch_us(torch, stream, launch, L)
     b = valid * (GATHER_READ_BYTES_PER_TOKEN + GATHER_WRITE_BYTES_PER_TOKEN)
     return {"kernel": "gather_kernel", "tokens": T, "avg_launch_us": round(us, 3), "alg_bytes": b,
             "gbps": round(b / (us * 1e-6) / 1e9, 1), "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "tokens_per_s": round(valid / (us * 1e-6), 1), "cold_launch_us": round(cold, 3),
-            "how": "eager back-to-back launches over the 61 layer caches of replica 0 (warm), and single "
-                   "launches after a 1 GiB scratch write (cold); bytes = 788 B read + 1408 B written per token"}
+            "tokens_per_s": round(valid / (us * 1e-6), 1), "eager_launch_us": round(eager_us, 3),
+            "cold_launch_us": round(cold, 3),
+            "how": "replays of a graph of 61 gathers over the 61 layer caches of replica 0 (avg), the same "
+                   "launches eagerly back to back (eager, host launch cost included), and single launches "
+                   "after a 1 GiB scratch write (cold); bytes = 788 B read + 1408 B written per token"}
 
 
 def cold_launch_us(torch, stream, launch, copies, n=12):
