@@ -182,8 +182,9 @@ KVPUB_API kvpub_status kvpub_store(kvpub_ctx *ctx, uint32_t layer, int64_t num_t
  * context poisoned by a fence timeout still gathers (reading publishes
  * nothing).  num_tokens == 0 returns KVPUB_OK and launches nothing.  No
  * allocation and no synchronization: safe under stream capture.  Argument
- * problems (replica >= R, layer >= L, bad pointers or strides) return
- * KVPUB_ERR_INVALID_ARG before anything is launched. */
+ * problems (replica >= R, layer >= L, bad pointers or strides, or a context
+ * with no backed pages -- see kvpub_vmm_grow) return KVPUB_ERR_INVALID_ARG
+ * before anything is launched. */
 KVPUB_API kvpub_status kvpub_gather(kvpub_ctx *ctx, uint32_t replica, uint32_t layer, int64_t num_tokens,
                                     const int64_t *slot_mapping, void *latent_out, int64_t latent_row_stride,
                                     void *rope_out, int64_t rope_row_stride, void *indexer_out,
@@ -216,8 +217,9 @@ KVPUB_API kvpub_status kvpub_vmm_create(kvpub_config *cfg, uint64_t max_pages, v
  * for use during stream capture or concurrently with launches on ctx from
  * another thread.  On failure the page count stays as it was, except in the
  * unlikely case that a layer's old backing could not be restored either:
- * then the storage reports 0 pages, ctx (if given) accepts no slot any more,
- * and KVPUB_ERR_HIP is returned.  Growing copies each layer's backed bytes
+ * then the storage reports 0 pages, ctx (if given) accepts no slot any more
+ * (stores count every slot as invalid, gathers are refused), and
+ * KVPUB_ERR_HIP is returned.  Growing copies each layer's backed bytes
  * once (the addresses stay, the physical memory behind them is replaced). */
 KVPUB_API kvpub_status kvpub_vmm_grow(kvpub_vmm *vmm, uint64_t num_pages, kvpub_ctx *ctx);
 
@@ -257,7 +259,8 @@ typedef struct {
  * (on a private stream) and instantiate it.  The graph binds the pointers in
  * io: to publish new data, rewrite those buffers before a replay.  They must
  * outlive the graph.  Argument checks as for kvpub_store, done for every layer
- * before capture begins. */
+ * before capture begins.  Captures on the context's private stream: create
+ * graphs of one context from one thread at a time. */
 KVPUB_API kvpub_status kvpub_graph_create(kvpub_ctx *ctx, const kvpub_layer_io *io, uint32_t n,
                                 uint32_t lane, kvpub_graph **out);
 

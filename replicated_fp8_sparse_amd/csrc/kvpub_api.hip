@@ -303,6 +303,9 @@ KVPUB_API kvpub_status kvpub_gather(kvpub_ctx* ctx, uint32_t replica, uint32_t l
                                     void* rope_out, int64_t rope_row_stride, void* indexer_out,
                                     int64_t indexer_row_stride, kvpub_stream_t stream) {
     if (!ctx || replica >= ctx->cfg.num_replicas) return KVPUB_ERR_INVALID_ARG;
+    // the kernel reads slot 0's bytes for every padded or out-of-range slot, so
+    // at least one page must be backed (a VMM storage that lost a layer has none)
+    if (ctx->cfg.num_pages == 0) return KVPUB_ERR_INVALID_ARG;
     // the outputs obey the same pointer, alignment and stride rules as the store's inputs
     kvpub_status st = check_store(ctx, layer, num_tokens, latent_out, latent_row_stride, rope_out,
                                   rope_row_stride, indexer_out, indexer_row_stride, slot_mapping);

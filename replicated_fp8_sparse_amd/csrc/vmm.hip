@@ -22,6 +22,7 @@
 // chunk is released only once the new one is in place and accessible (on any
 // failure the old one is put back).  Every chunk's access flags are read back
 // before it is handed out.
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -88,8 +89,23 @@ hipError_t map_rw(int device, uint8_t* ptr, size_t bytes, hipMemGenericAllocatio
     return e;
 }
 
+// Test hook for the failure paths of growing: KVPUB_TEST_VMM_GROW_FAIL=swap
+// makes mapping the bigger chunk at the layer's address fail (the old chunk is
+// put back); =restore makes putting the old chunk back fail as well (the
+// storage becomes broken).  Read at every grow, host side only.
+struct GrowFailHook {
+    bool swap = false, restore = false;
+    GrowFailHook() {
+        const char* s = std::getenv("KVPUB_TEST_VMM_GROW_FAIL");
+        if (!s) return;
+        restore = std::strcmp(s, "restore") == 0;
+        swap = restore || std::strcmp(s, "swap") == 0;
+    }
+};
+
 // Back layer (a, r, l) with `bytes` (> what it has), keeping its contents.
 hipError_t grow_layer(kvpub_vmm* v, int a, uint32_t r, uint32_t l, size_t bytes, uint8_t* scratch) {
+    const GrowFailHook hook;
     Chunk& old = v->at(a, r, l);
     uint8_t* ptr = v->layer_ptr(a, r, l);
     const hipMemAllocationProp prop = device_prop(v->device);
@@ -106,11 +122,11 @@ hipError_t grow_layer(kvpub_vmm* v, int a, uint32_t r, uint32_t l, size_t bytes,
         if (e == hipSuccess) e = hipMemUnmap(ptr, old.bytes);
         if (e != hipSuccess) { (void)hipMemRelease(h); return e; }
     }
-    e = map_rw(v->device, ptr, bytes, h);
+    e = hook.swap ? hipErrorInvalidValue : map_rw(v->device, ptr, bytes, h);
     if (e != hipSuccess) {
         (void)hipMemRelease(h);
         // put the old chunk back; if even that fails the layer is unbacked
-        if (old.bytes && map_rw(v->device, ptr, old.bytes, old.handle) != hipSuccess) {
+        if (old.bytes && (hook.restore || map_rw(v->device, ptr, old.bytes, old.handle) != hipSuccess)) {
             (void)hipMemRelease(old.handle);
             old = Chunk{0, hipMemGenericAllocationHandle_t{}};
             v->broken = true;

@@ -144,3 +144,80 @@ def test_vmm_bad_arguments():
         assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, 8)
     finally:
         kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
+
+
+def _grow_forced_to_fail(mode, vmm, pages, ctx, monkeypatch):
+    monkeypatch.setenv("KVPUB_TEST_VMM_GROW_FAIL", mode)
+    try:
+        return kvpub.kvpub_vmm_grow(vmm, pages, ctx)
+    finally:
+        monkeypatch.delenv("KVPUB_TEST_VMM_GROW_FAIL")
+
+
+def test_vmm_failed_grow_keeps_the_storage(orc, monkeypatch):
+    """Mapping the bigger chunk fails (forced from the host): the old chunk is put
+    back, the page count and every written byte stay, and the storage grows later."""
+    G.log("vmm: forced swap failure, R=1, L=2, 16 -> 64 pages")
+    t = G.torch()
+    hip = G.hip_runtime()
+    R, L, P0, P1 = 1, 2, 16, 64
+    cfg = kvpub.kvpub_config_init(R, L, P0)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, 128)
+    kvpub.check(st, "kvpub_vmm_create")
+    try:
+        fill_pages(hip, cfg, mb, ib, 0, P0, L)
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st)
+        mirror = Mirror(cfg, L)
+        rng = np.random.default_rng(52)
+        x = W.LayerInputs(*W._normal_rows(rng, 300), rng.permutation(P0 * 64)[:300].astype(np.int64))
+        d = G.DeviceInputs(x)
+        s = t.cuda.current_stream().cuda_stream
+        kvpub.check(kvpub.kvpub_store(ctx, 1, d.T, d.latent.data_ptr(), 512, d.rope.data_ptr(), 64,
+                                      d.indexer.data_ptr(), 128, d.slots.data_ptr(), s))
+        t.cuda.synchronize()
+        mirror.store(orc, P0, 1, x)
+        assert _grow_forced_to_fail("swap", vmm, P1, ctx, monkeypatch) == kvpub.KVPUB_ERR_HIP
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, P0)
+        compare_backed(hip, cfg, mb, ib, mirror, P0, L, "after a failed grow")
+        kvpub.check(kvpub.kvpub_vmm_grow(vmm, P1, ctx), "kvpub_vmm_grow")
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, P1)
+        compare_backed(hip, cfg, mb, ib, mirror, P0, L, "after growing")
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
+
+
+def test_vmm_broken_storage_fails_closed(monkeypatch):
+    """Mapping the bigger chunk and putting the old one back both fail (forced from
+    the host): the storage and its context report 0 pages, stores count every slot
+    as invalid and write nothing, gathers are refused, and destroy still works."""
+    G.log("vmm: forced swap + restore failure, R=2, L=2, 8 -> 32 pages")
+    t = G.torch()
+    R, L, P0 = 2, 2, 8
+    cfg = kvpub.kvpub_config_init(R, L, P0)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, 64)
+    kvpub.check(st, "kvpub_vmm_create")
+    try:
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st)
+        assert _grow_forced_to_fail("restore", vmm, 32, ctx, monkeypatch) == kvpub.KVPUB_ERR_HIP
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, 0)
+        assert kvpub.kvpub_vmm_grow(vmm, 32, ctx) == kvpub.KVPUB_ERR_HIP     # stays broken
+        rng = np.random.default_rng(53)
+        x = W.LayerInputs(*W._normal_rows(rng, 100), rng.permutation(P0 * 64)[:100].astype(np.int64))
+        d = G.DeviceInputs(x)
+        s = t.cuda.current_stream().cuda_stream
+        for layer in range(L):
+            kvpub.check(kvpub.kvpub_store(ctx, layer, d.T, d.latent.data_ptr(), 512, d.rope.data_ptr(), 64,
+                                          d.indexer.data_ptr(), 128, d.slots.data_ptr(), s))
+        t.cuda.synchronize()
+        st, invalid, _ = kvpub.kvpub_error_read(ctx, True)
+        kvpub.check(st)
+        assert invalid == L * 100
+        out = [t.zeros((100, w), dtype=t.int16, device="cuda") for w in (512, 64, 128)]
+        assert kvpub.kvpub_gather(ctx, 0, 0, 100, d.slots.data_ptr(), out[0].data_ptr(), 512, out[1].data_ptr(),
+                                  64, out[2].data_ptr(), 128, s) == kvpub.KVPUB_ERR_INVALID_ARG
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
