@@ -16,7 +16,9 @@
 // slot 0's bytes (always in bounds, so no load sits behind a branch) and its
 // output row is written as zeros.  Decode: the gfx950 OCP e4m3 -> f32 convert
 // (exact), one binary32 multiply by the tile scale, a round-to-nearest-even
-// f32 -> bf16 convert; each lane stores 8 bf16 = 16 bytes.
+// f32 -> bf16 convert; each lane stores 8 bf16 = 16 bytes.  Every output line
+// is written whole, so the stores stream past L2 (non-temporal): nothing is
+// left dirty for the end-of-kernel write-back.
 #include "kvpub_internal.h"
 
 namespace kvpub {
@@ -70,6 +72,11 @@ __device__ __forceinline__ uint64_t pick4(uint64_t v0, uint64_t v1, uint64_t v2,
     const uint64_t a = (i & 1u) ? v1 : v0;
     const uint64_t b = (i & 1u) ? v3 : v2;
     return (i & 2u) ? b : a;
+}
+
+template <class T>
+__device__ __forceinline__ void st_nt(uint16_t* p, T v) {
+    __builtin_nontemporal_store(v, (gptr<T>)p);
 }
 
 template <class T>
@@ -130,15 +137,15 @@ __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
     for (int k = 0; k < 4; ++k) {
         if (t0 + k > last) break;                // uniform: the tail of the last group
         const u32x4 v = ((ok >> k) & 1u) ? dequant8(code[k], scale[k]) : zero;
-        *(gptr<u32x4>)(p.latent + (uint64_t)(t0 + k) * p.latent_stride + lane * 8u) = v;
+        st_nt<u32x4>(p.latent + (uint64_t)(t0 + k) * p.latent_stride + lane * 8u, v);
     }
     if (t0 + g <= last) {
         const u32x4 v = ((ok >> g) & 1u) ? dequant8(code[4], scale[4]) : zero;
-        *(gptr<u32x4>)(p.indexer + (uint64_t)(t0 + g) * p.indexer_stride + (lane & 15u) * 8u) = v;
+        st_nt<u32x4>(p.indexer + (uint64_t)(t0 + g) * p.indexer_stride + (lane & 15u) * 8u, v);
     }
     if (lane < 32u && t0 + r <= last) {
         const u32x4 v = ((ok >> r) & 1u) ? rp : zero;
-        *(gptr<u32x4>)(p.rope + (uint64_t)(t0 + r) * p.rope_stride + (lane & 7u) * 8u) = v;
+        st_nt<u32x4>(p.rope + (uint64_t)(t0 + r) * p.rope_stride + (lane & 7u) * 8u, v);
     }
 }
 
