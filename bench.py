@@ -224,7 +224,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "store_kernel<2, true>",
+            "kernel": "store_kernel<2, true, false>",
             "achieved": round(store_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -150,6 +150,13 @@ StoreParams store_params(kvpub_ctx* ctx, uint32_t layer, int64_t T, const void* 
     }
     p.invalid_count = reinterpret_cast<unsigned long long*>(ctx->words + kvpub::kInvalidOffset);
     p.status = reinterpret_cast<const uint32_t*>(ctx->words + kvpub::kStatusOffset);
+    // a layer of one replica in 32-bit offsets (the write-through store path)?
+    const uint64_t main_region = ctx->cfg.num_pages * ctx->cfg.main_page_stride;
+    const uint64_t idx_region = ctx->cfg.num_pages * ctx->cfg.idx_page_stride;
+    if (main_region <= UINT32_MAX && idx_region <= UINT32_MAX) {
+        p.main_region = (uint32_t)main_region;
+        p.idx_region = (uint32_t)idx_region;
+    }
     return p;
 }
 

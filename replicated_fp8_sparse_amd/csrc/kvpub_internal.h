@@ -43,6 +43,8 @@ struct StoreParams {
     uint8_t* idx_base[kMaxReplicas];
     unsigned long long* invalid_count;
     const uint32_t* status;
+    uint32_t main_region;        // bytes of one replica's layer (num_pages * page stride) if below
+    uint32_t idx_region;         // 2^32, else 0: the write-through path needs 32-bit offsets
 };
 
 struct FenceParams {

@@ -33,9 +33,9 @@
 // gfx950 OCP e4m3 convert (round-to-nearest-even, saturating only above 464):
 // |x/scale| <= 448 (1 + 2^-23) for finite input, so no clamp is needed.
 //
-// Every piece is stored straight to its slot in each replica (ordinary
-// write-back stores, so neighbouring pieces of a 128-byte line merge in L2);
-// the inputs are read with non-temporal loads (read once, never reused).
+// Every piece is stored straight to its slot in each replica; the inputs are
+// read with non-temporal loads (read once, never reused).  How the stores
+// treat the L2 depends on the launch size (see put_at).
 #include "kvpub_internal.h"
 
 namespace kvpub {
@@ -52,15 +52,45 @@ template <class T> using lptr = __attribute__((address_space(3))) T*;
 constexpr uint32_t kRunBytes = 4 * 656;   // 2624 = 164 x 16 B
 constexpr int64_t kCacheBytesPerToken = 656 + 128 + 4;              // per replica
 constexpr int64_t kStreamingStoreBytes = int64_t(16) << 20;         // launches writing at most this stream
+constexpr int64_t kWriteThroughBytes = int64_t(32) << 20;           // more than the 8 L2s hold: write through
 
-// Whole-line pieces (row runs, Indexer-K codes) of a small launch are stored
-// non-temporally: nothing of them is left dirty in L2 for the end-of-kernel
-// write-back, which a latency-bound launch would otherwise wait for.  Large
-// launches keep write-back stores, whose merging in L2 pays at full bandwidth.
+// Store policy by launch size:
+//   NT (a launch writing at most kStreamingStoreBytes): whole-line pieces (row
+//     runs, Indexer-K codes) are stored non-temporally, the partial pieces with
+//     ordinary write-back stores.  Nothing of the whole lines is left dirty in
+//     L2 for the end-of-kernel write-back, which a latency-bound launch would
+//     otherwise wait for, while the partial lines still merge in L2.
+//   WT (a launch writing more than kWriteThroughBytes, more than the eight
+//     4 MB L2s can hold): every piece is a buffer store with the device-
+//     coherence bit, written through this XCD's L2 instead of held dirty in
+//     it, so the writes stream out while the kernel runs instead of being
+//     evicted later.  Buffer offsets are 32-bit, so WT needs each replica's
+//     layer to span less than 2^32 bytes; the buffer's range check
+//     (num_records = the layer's size) drops any store outside the layer.
+//   otherwise (launches in between, or layers too large for WT): ordinary
+//     write-back stores, which the L2s absorb.
 template <bool NT, class T>
 __device__ __forceinline__ void put(gptr<T> p, T v) {
     if (NT) __builtin_nontemporal_store(v, p);
     else *p = v;
+}
+
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data format (gfx950)
+constexpr int kDeviceCoherent = 16;      // buffer cache-policy bits: sc1
+
+// Store v at base + off: `whole` marks a piece that covers whole 128-byte lines.
+template <bool NT, bool WT, bool whole, class T>
+__device__ __forceinline__ void put_at(gbyte* base, uint32_t region, uint64_t off, T v) {
+    if constexpr (WT) {
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)region, kRsrcWord3);
+        const int o = (int)(uint32_t)off;
+        if constexpr (sizeof(T) == 16) __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, kDeviceCoherent);
+        else if constexpr (sizeof(T) == 8) __builtin_amdgcn_raw_buffer_store_b64(v, r, o, 0, kDeviceCoherent);
+        else __builtin_amdgcn_raw_buffer_store_b32(v, r, o, 0, kDeviceCoherent);
+    } else {
+        put<NT && whole>((gptr<T>)(base + off), v);
+    }
 }
 
 constexpr float kE4m3Max = 448.0f;
@@ -270,9 +300,9 @@ __device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2,
 //   Indexer-K scale   -> page bytes [8192 + 4*(slot%64), +4) (lane 16g)
 // The five rounds are computed as one straight-line block (their reductions
 // and scale sequences interleave); only the stores are conditional.
-template <int R, bool NT>
+template <int R, bool NT, bool WT>
 __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, const Bases<R>& b, uint32_t lane,
-                                               lbyte* img) {
+                                               lbyte* img, uint32_t main_region, uint32_t idx_region) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
 #pragma unroll
@@ -333,10 +363,10 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, co
         const u32x4 c2 = lane < 36u ? *(lptr<u32x4>)(img + 2048u + lane * 16u) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            gbyte* run0 = b.main[r] + d.row[0];
-            put<NT>((gptr<u32x4>)(run0 + lane * 16u), c0);
-            put<NT>((gptr<u32x4>)(run0 + 1024u + lane * 16u), c1);
-            if (lane < 36u) put<NT>((gptr<u32x4>)(run0 + 2048u + lane * 16u), c2);
+            const uint64_t o = d.row[0] + lane * 16u;
+            put_at<NT, WT, true>(b.main[r], main_region, o, c0);
+            put_at<NT, WT, true>(b.main[r], main_region, o + 1024u, c1);
+            if (lane < 36u) put_at<NT, WT, true>(b.main[r], main_region, o + 2048u, c2);
         }
     } else {
         // A tile's scale is the same in all 16 lanes of its row; the 16 lanes
@@ -346,21 +376,21 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, co
             if (!((d.tok >> k) & 1u)) continue;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                gbyte* row = b.main[r] + d.row[k];
-                *(gptr<u32x2>)(row + lane * 8u) = codes[k];
-                *(gptr<uint32_t>)(row + 512u + (lane >> 4) * 4u) = __float_as_uint(scale[k]);
+                put_at<NT, WT, false>(b.main[r], main_region, d.row[k] + lane * 8u, codes[k]);
+                put_at<NT, WT, false>(b.main[r], main_region, d.row[k] + 512u + (lane >> 4) * 4u,
+                                      __float_as_uint(scale[k]));
             }
         }
         if (d.ok_r) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) *(gptr<u32x4>)(b.main[r] + d.rope) = G.rp;
+            for (int r = 0; r < R; ++r) put_at<NT, WT, false>(b.main[r], main_region, d.rope, G.rp);
         }
     }
     if (d.ok_g) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            put<NT>((gptr<u32x2>)(b.idx[r] + d.icode), codes[4]);
-            *(gptr<uint32_t>)(b.idx[r] + d.iscale) = __float_as_uint(scale[4]);
+            put_at<NT, WT, true>(b.idx[r], idx_region, d.icode, codes[4]);
+            put_at<NT, WT, false>(b.idx[r], idx_region, d.iscale, __float_as_uint(scale[4]));
         }
     }
 }
@@ -395,7 +425,7 @@ __device__ __forceinline__ void fetch_rows(const uint16_t* latent, const uint16_
 // instructions need: they arrive preloaded in SGPRs (kernel-argument
 // preloading); p is fetched while the row loads are in flight.  Token
 // indices are 32-bit (a launch holds at most kMaxTokensPerLaunch tokens).
-template <int R, bool NT>
+template <int R, bool NT, bool WT>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
@@ -428,25 +458,25 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const Bases<R> b = pin_bases<R>(p);
     const Dest d = destinations(sl[0], sl[1], sl[2], sl[3], poisoned, lane, p);
     __builtin_amdgcn_sched_barrier(0);
-    quantize_store<R, NT>(G, d, b, lane, (lbyte*)&run_img[wave][0]);
+    quantize_store<R, NT, WT>(G, d, b, lane, (lbyte*)&run_img[wave][0], p.main_region, p.idx_region);
 }
 
 }  // namespace
 
-template <bool NT>
+template <bool NT, bool WT>
 static void launch_r(uint32_t num_replicas, dim3 grid, dim3 block, hipStream_t stream, const uint16_t* lat,
                      const uint16_t* rp, const uint16_t* ix, const int64_t* sl, uint32_t n, const StoreParams& p) {
 #define KVPUB_ROW_ARGS lat, rp, ix, sl, n, (uint32_t)p.latent_stride, (uint32_t)p.rope_stride, \
     (uint32_t)p.indexer_stride, p.status, p
     switch (num_replicas) {
-        case 1: store_kernel<1, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 2: store_kernel<2, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 3: store_kernel<3, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 4: store_kernel<4, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 5: store_kernel<5, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 6: store_kernel<6, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 7: store_kernel<7, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        default: store_kernel<8, NT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 1: store_kernel<1, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 2: store_kernel<2, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 3: store_kernel<3, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 4: store_kernel<4, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 5: store_kernel<5, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 6: store_kernel<6, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 7: store_kernel<7, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        default: store_kernel<8, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
     }
 #undef KVPUB_ROW_ARGS
 }
@@ -464,9 +494,14 @@ hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t
         const uint16_t* rp = p.rope + t * p.rope_stride;
         const uint16_t* ix = p.indexer + t * p.indexer_stride;
         const int64_t* sl = p.slots + t;
-        const bool small = n * (int64_t)num_replicas * kCacheBytesPerToken <= kStreamingStoreBytes;
-        if (small) launch_r<true>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
-        else launch_r<false>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
+        const int64_t written = n * (int64_t)num_replicas * kCacheBytesPerToken;
+        const bool offsets32 = p.main_region != 0 && p.idx_region != 0;
+        if (written <= kStreamingStoreBytes)
+            launch_r<true, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
+        else if (written > kWriteThroughBytes && offsets32)
+            launch_r<false, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
+        else
+            launch_r<false, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

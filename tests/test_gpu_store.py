@@ -334,3 +334,40 @@ def test_store_across_the_launch_split(orc):
         assert np.array_equal(got_idx[i], want_i), f"split gather indexer, token {sample[i]}"
     del g_lat, g_rope, g_idx
     dev.free()
+
+
+@pytest.mark.parametrize("R,T", [(3, 15003), (4, 13001)])
+def test_write_through_scattered_slots(orc, R, T):
+    """A launch that writes more than 32 MB takes the write-through store path.
+    Most slots are scattered (no row runs, so every piece goes through the
+    per-token stores), 40 pages are filled by consecutive runs, and there are
+    pads, invalid slots, all-zero rows and a ragged tail.  Every written row,
+    the invalid count, and every byte outside the rows (guards included) are
+    checked against the oracle."""
+    rng = np.random.default_rng(61 + R)
+    layout = CacheLayout(replicas=R, layers=1, num_pages=4096, guard=64)
+    assert T * R * 788 > 32 << 20
+    pages = rng.permutation(layout.num_pages)
+    run_slots = (64 * pages[:40, None] + np.arange(64)).reshape(-1)
+    rest = (64 * pages[40:, None] + np.arange(64)).reshape(-1)
+    scattered = rng.choice(rest, size=T - run_slots.size, replace=False)
+    slots = np.concatenate([run_slots, scattered]).astype(np.int64)
+    slots[::23] = -1
+    slots[[7, 1001, T - 2]] = [layout.capacity + 3, 2 * layout.capacity, -9]
+    lat, rope, ind = W._normal_rows(rng, T)
+    lat[[11, 2600]] = 0
+    ind[[12, T - 1]] = 0
+    x = LayerInputs(lat, rope, ind, slots)
+    G.log(f"write-through scattered: R={R} T={T}")
+    dev = G.DeviceCache(layout)
+    try:
+        kvpub.check(dev.store(0, G.DeviceInputs(x)), "kvpub_store")
+        st, invalid, flags = dev.errors()
+        kvpub.check(st, "kvpub_error_read")
+        assert invalid == 3 and flags == 0
+        rows = G.oracle_rows_parallel(orc, x)
+        G.assert_gathered_parity(dev, 0, x, rows, "write-through scattered")
+        G.assert_replicas_identical(dev)
+        G.assert_untouched(dev, [(0, x.slots)])
+    finally:
+        dev.free()
