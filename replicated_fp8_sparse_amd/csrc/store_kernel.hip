@@ -53,6 +53,9 @@ constexpr uint32_t kRunBytes = 4 * 656;   // 2624 = 164 x 16 B
 constexpr int64_t kCacheBytesPerToken = 656 + 128 + 4;              // per replica
 constexpr int64_t kStreamingStoreBytes = int64_t(16) << 20;         // launches writing at most this stream
 constexpr int64_t kWriteThroughBytes = int64_t(32) << 20;           // more than the 8 L2s hold: write through
+// Batches up to this many tokens take small_store_kernel (up to twice as many
+// with one or two replicas): measured crossover against the main kernel.
+constexpr int64_t kSmallBatchTokens = 1024;
 
 // Store policy by launch size:
 //   NT (a launch writing at most kStreamingStoreBytes): whole-line pieces (row
@@ -461,6 +464,92 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     quantize_store<R, NT, WT>(G, d, b, lane, (lbyte*)&run_img[wave][0], p.main_region, p.idx_region);
 }
 
+// Small batches (a decode step: tens of tokens; up to about a thousand).
+// The launch is latency-bound there, and a wave's five rounds of arithmetic
+// sit on its critical path, so the rounds of a group are spread over five
+// waves instead: one block per group of 4 tokens, wave k < 4 takes token k's
+// latent row (its four tiles) and, in lanes 0..7, its RoPE; wave 4 takes the
+// four tokens' Indexer-K rows.  Same per-tile arithmetic as the main kernel;
+// ordinary write-back stores, one row at a time (no row-run image: at larger
+// batches the main kernel's merged run stores win).
+constexpr int kSmallWaves = 5;
+
+template <int R>
+__global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
+    const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
+    const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
+    uint32_t indexer_stride, const uint32_t* __restrict__ status, const StoreParams p) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t round = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..4
+    const uint32_t t0 = blockIdx.x * kTokensPerWave;
+    const uint32_t last = num_tokens - 1;
+    int64_t sl[4];
+    fetch_slots(slots, t0, last, sl);
+    const uint32_t st = *status;
+    u32x4 row, rp = u32x4{0u, 0u, 0u, 0u};
+    if (round < 4) {
+        const uint32_t t = t0 + round < last ? t0 + round : last;
+        rp = ld16(rope + (uint64_t)t * rope_stride + (lane & 7u) * 8u);
+        row = ld16(latent + (uint64_t)t * latent_stride + lane * 8u);
+    } else {
+        const uint32_t ug = t0 + (lane >> 4), tg = ug < last ? ug : last;
+        row = ld16(indexer + (uint64_t)tg * indexer_stride + (lane & 15u) * 8u);
+    }
+    const bool poisoned = (st & kStatusPoisoned) != 0;
+    uint32_t nbad = 0, tok = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        sl[k] = t0 + k <= last ? sl[k] : -1;
+        const bool good = slot_ok(sl[k], p.capacity);
+        nbad += (sl[k] != -1 && !good) ? 1u : 0u;
+        tok |= (!poisoned && good) ? (1u << k) : 0u;
+    }
+    if (round == 0 && nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
+
+    const uint32_t ab = row_max16(lane_amax_bits(row));
+    const uint32_t E = ab >> 7;
+    const bool f = E >= kFastMinExponent && E < 255u;
+    const TileScale t = tile_scale(ab);
+    float x[8], q[8];
+    unpack8(row, x);
+    float scale;
+    if (__all(f)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], t.s, t.y);
+        scale = t.s;
+    } else {
+        const float s_exact = __uint_as_float(ab << 16) / kE4m3Max;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[e], t.s, t.y) : quotient_exact(x[e], s_exact);
+        scale = f ? t.s : s_exact;
+    }
+    const u32x2 codes = cvt8(q);
+
+    if (round < 4) {
+        if (!((tok >> round) & 1u)) return;
+        const uint64_t s = (uint64_t)sl[round];
+        const uint64_t off = (s >> 6) * p.main_page_stride + (s & 63u) * 656u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            gbyte* rw = (gbyte*)p.main_base[r] + off;
+            *(gptr<u32x2>)(rw + lane * 8u) = codes;
+            *(gptr<uint32_t>)(rw + 512u + (lane >> 4) * 4u) = __float_as_uint(scale);
+            if (lane < 8u) *(gptr<u32x4>)(rw + 528u + lane * 16u) = rp;
+        }
+    } else {
+        const uint32_t g = lane >> 4;
+        if (!((tok >> g) & 1u)) return;
+        const uint64_t s = (uint64_t)(g == 0 ? sl[0] : g == 1 ? sl[1] : g == 2 ? sl[2] : sl[3]);
+        const uint64_t page = (s >> 6) * p.idx_page_stride, in = s & 63u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            gbyte* ib = (gbyte*)p.idx_base[r] + page;
+            *(gptr<u32x2>)(ib + in * 128u + (lane & 15u) * 8u) = codes;
+            *(gptr<uint32_t>)(ib + 8192u + in * 4u) = __float_as_uint(scale);
+        }
+    }
+}
+
 }  // namespace
 
 template <bool NT, bool WT>
@@ -481,11 +570,32 @@ static void launch_r(uint32_t num_replicas, dim3 grid, dim3 block, hipStream_t s
 #undef KVPUB_ROW_ARGS
 }
 
+static void launch_small(uint32_t num_replicas, uint32_t n, hipStream_t stream, const StoreParams& p) {
+    const dim3 grid((n + kTokensPerWave - 1) / kTokensPerWave), block(kSmallWaves * 64);
+#define KVPUB_ROW_ARGS p.latent, p.rope, p.indexer, p.slots, n, (uint32_t)p.latent_stride, \
+    (uint32_t)p.rope_stride, (uint32_t)p.indexer_stride, p.status, p
+    switch (num_replicas) {
+        case 1: small_store_kernel<1><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 2: small_store_kernel<2><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 3: small_store_kernel<3><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 4: small_store_kernel<4><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 5: small_store_kernel<5><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 6: small_store_kernel<6><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 7: small_store_kernel<7><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        default: small_store_kernel<8><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+    }
+#undef KVPUB_ROW_ARGS
+}
+
 hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream) {
     if (num_replicas < 1 || num_replicas > (uint32_t)kMaxReplicas) return hipErrorInvalidValue;
     // One wave per group of 4 tokens; batches beyond kMaxTokensPerLaunch are
     // split so that the grid stays far inside its limits.
     (void)hipGetLastError();
+    if (p.num_tokens <= (num_replicas <= 2 ? 2 * kSmallBatchTokens : kSmallBatchTokens)) {
+        launch_small(num_replicas, (uint32_t)p.num_tokens, stream, p);
+        return hipGetLastError();
+    }
     for (int64_t t = 0; t < p.num_tokens; t += kMaxTokensPerLaunch) {
         const int64_t n = p.num_tokens - t < kMaxTokensPerLaunch ? p.num_tokens - t : kMaxTokensPerLaunch;
         const uint32_t blocks = (uint32_t)((n + kTokensPerBlock - 1) / kTokensPerBlock);

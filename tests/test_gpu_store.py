@@ -46,9 +46,33 @@ def run_full(orc, layout, layer_inputs, label):
         dev.free()
 
 
-def test_tiny_parity(orc):
+# Batches of up to 1024 tokens (2048 with one or two replicas) take the
+# small-batch mapping (one wave per group and round); larger ones the main
+# kernel.  Appending this many padded tokens (slot -1: nothing written) runs a
+# small case through the main kernel with the same expected bytes.
+MAIN_KERNEL_PADS = 2100
+MAPPINGS = ["small", "main"]
+
+
+def with_pads(x, n, rng):
+    """x followed by n padded tokens with random rows."""
+    if n == 0:
+        return x
+    extra = lambda w: bf16_bits(rng.standard_normal((n, w)).astype(np.float32))
+    return LayerInputs(np.concatenate([x.latent, extra(512)]), np.concatenate([x.rope, extra(64)]),
+                       np.concatenate([x.indexer, extra(128)]),
+                       np.concatenate([x.slots, np.full(n, -1, np.int64)]))
+
+
+def pads_for(mapping):
+    return MAIN_KERNEL_PADS if mapping == "main" else 0
+
+
+@pytest.mark.parametrize("mapping", MAPPINGS)
+def test_tiny_parity(orc, mapping):
     layout, x = W.tiny()
-    run_full(orc, layout, [(0, x)], "tiny T=256")
+    x = with_pads(x, pads_for(mapping), np.random.default_rng(7))
+    run_full(orc, layout, [(0, x)], f"tiny T=256 ({mapping} mapping)")
 
 
 def _hand_rows(rng):
@@ -94,7 +118,8 @@ def _hand_rows(rng):
     return rows
 
 
-def test_hand_cases_parity(orc):
+@pytest.mark.parametrize("mapping", MAPPINGS)
+def test_hand_cases_parity(orc, mapping):
     rng = np.random.default_rng(101)
     rows = _hand_rows(rng)
     n = len(rows)
@@ -112,10 +137,12 @@ def test_hand_cases_parity(orc):
     slots[n + 2] = 2 ** 40
     slots[n + 3] = -7
     slots[n + 4:] = -1
-    run_full(orc, layout, [(1, LayerInputs(latent, rope, indexer, slots))], f"hand cases T={T}")
+    x = with_pads(LayerInputs(latent, rope, indexer, slots), pads_for(mapping), rng)
+    run_full(orc, layout, [(1, x)], f"hand cases T={T} ({mapping} mapping)")
 
 
-def test_encoder_sweep_parity(orc):
+@pytest.mark.parametrize("mapping", MAPPINGS)
+def test_encoder_sweep_parity(orc, mapping):
     """Tiles with amax 448 have scale 1.0, so every bf16 value in [-448, 448] is
     fed to the e4m3 conversion exactly once."""
     b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
@@ -139,26 +166,32 @@ def test_encoder_sweep_parity(orc):
     rope = rng.integers(0, 65536, size=(n_tok, 64), dtype=np.uint16)
     layout = CacheLayout(replicas=1, layers=1, num_pages=4)
     slots = rng.permutation(layout.capacity)[:n_tok].astype(np.int64)
-    run_full(orc, layout, [(0, LayerInputs(latent, rope, indexer, slots))], f"encoder sweep T={n_tok}")
+    x = with_pads(LayerInputs(latent, rope, indexer, slots), pads_for(mapping), rng)
+    run_full(orc, layout, [(0, x)], f"encoder sweep T={n_tok} ({mapping} mapping)")
 
 
+@pytest.mark.parametrize("mapping", MAPPINGS)
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 7, 13, 17, 31, 33, 63, 65, 100, 1001])
-def test_ragged_and_strided(orc, T):
+def test_ragged_and_strided(orc, T, mapping):
     """Token counts that leave partial waves and blocks; inputs with row strides
-    wider than the rows; three replicas."""
+    wider than the rows; three replicas.  With the main mapping, padded tokens
+    follow the T real ones (the same partial groups, in a larger launch)."""
     import torch
     rng = np.random.default_rng(200 + T)
     layout = CacheLayout(replicas=3, layers=1, num_pages=32)
     LS, RS, IS = 520, 72, 136
+    T_real = T
+    T = T_real + pads_for(mapping)
     wide_l = bf16_bits(rng.standard_normal((T, LS)).astype(np.float32))
     wide_r = bf16_bits(rng.standard_normal((T, RS)).astype(np.float32))
     wide_i = bf16_bits(rng.standard_normal((T, IS)).astype(np.float32))
-    slots = rng.permutation(layout.capacity)[:T].astype(np.int64)
-    if T > 4:
-        slots[rng.choice(T, T // 5, replace=False)] = -1
+    slots = np.full(T, -1, np.int64)
+    slots[:T_real] = rng.permutation(layout.capacity)[:T_real]
+    if T_real > 4:
+        slots[rng.choice(T_real, T_real // 5, replace=False)] = -1
     x = LayerInputs(np.ascontiguousarray(wide_l[:, :512]), np.ascontiguousarray(wide_r[:, :64]),
                     np.ascontiguousarray(wide_i[:, :128]), slots)
-    G.log(f"ragged T={T} strides {LS}/{RS}/{IS}")
+    G.log(f"ragged T={T_real} strides {LS}/{RS}/{IS} ({mapping} mapping, launch of {T})")
     dev = G.DeviceCache(layout)
     try:
         dl, dr, di = G.to_dev_u16(wide_l), G.to_dev_u16(wide_r), G.to_dev_u16(wide_i)
@@ -266,11 +299,13 @@ def _run_slots(rng, T, capacity, kind):
     raise ValueError(kind)
 
 
+@pytest.mark.parametrize("mapping", MAPPINGS)
 @pytest.mark.parametrize("T", [8, 16, 17, 40, 63, 1000])
 @pytest.mark.parametrize("kind", ["from0", "offset3", "offset61", "reversed", "holes", "pages"])
-def test_consecutive_slot_runs(orc, T, kind):
-    """Slot runs (the row-image path) and broken runs (the piece-by-piece path)
-    in the same launch, two replicas, page guards."""
+def test_consecutive_slot_runs(orc, T, kind, mapping):
+    """Slot runs (the main kernel's row-image path) and broken runs (its
+    piece-by-piece path) in the same launch, two replicas, page guards; run
+    through both mappings (padded tokens appended for the main one)."""
     rng = np.random.default_rng(300 + T)
     layout = CacheLayout(replicas=2, layers=1, num_pages=24, guard=64)
     slots = _run_slots(rng, T, layout.capacity, kind)
@@ -278,7 +313,8 @@ def test_consecutive_slot_runs(orc, T, kind):
     rope = bf16_bits(rng.standard_normal((T, 64)).astype(np.float32))
     indexer = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32))
     latent[T // 2] = 0                   # an all-zero row inside a run
-    run_full(orc, layout, [(0, LayerInputs(latent, rope, indexer, slots))], f"runs {kind} T={T}")
+    x = with_pads(LayerInputs(latent, rope, indexer, slots), pads_for(mapping), rng)
+    run_full(orc, layout, [(0, x)], f"runs {kind} T={T} ({mapping} mapping)")
 
 
 def test_store_across_the_launch_split(orc):
