@@ -407,3 +407,37 @@ def test_write_through_scattered_slots(orc, R, T):
         G.assert_untouched(dev, [(0, x.slots)])
     finally:
         dev.free()
+
+
+def _mixed_slots(rng, T, num_pages):
+    """Half the tokens fill whole pages in a permuted order (row runs), the rest
+    take scattered slots of other pages; every 17th token is padded and two
+    slots are invalid."""
+    pages = rng.permutation(num_pages)
+    n_run = (T // 2) // 64 * 64
+    run = (64 * pages[:n_run // 64, None] + np.arange(64)).reshape(-1)
+    rest = (64 * pages[n_run // 64:, None] + np.arange(64)).reshape(-1)
+    slots = np.concatenate([run, rng.choice(rest, size=T - n_run, replace=False)]).astype(np.int64)
+    slots[3::17] = -1
+    slots[[1, T - 3]] = [64 * num_pages + 9, -2]
+    return slots
+
+
+@pytest.mark.parametrize("path", ["small", "main", "write_back", "write_through"])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_every_replica_count(orc, R, path):
+    """R = 1..8 through each store path: the small-batch mapping (300 tokens),
+    the main kernel with streamed whole lines (the same tokens behind padded
+    ones), with write-back stores (a batch writing about 24 MB) and with
+    write-through stores (just over 32 MB).  Whole buffers against the oracle."""
+    rng = np.random.default_rng(500 + R)
+    T = {"small": 300, "main": 300, "write_back": (24 << 20) // (R * 788),
+         "write_through": (32 << 20) // (R * 788) + 97}[path]
+    num_pages = max(16, 2 * ((T + 63) // 64))
+    layout = CacheLayout(replicas=R, layers=1, num_pages=num_pages, guard=64)
+    slots = _mixed_slots(rng, T, num_pages)
+    lat, rope, ind = W._normal_rows(rng, T)
+    x = LayerInputs(lat, rope, ind, slots)
+    if path == "main":
+        x = with_pads(x, MAIN_KERNEL_PADS, rng)
+    run_full(orc, layout, [(0, x)], f"R={R} {path} T={x.slots.size}")
