@@ -423,15 +423,15 @@ def _mixed_slots(rng, T, num_pages):
     return slots
 
 
-@pytest.mark.parametrize("path", ["small", "main", "write_back", "write_through"])
+@pytest.mark.parametrize("path", ["small", "small_max", "main", "write_back", "write_through"])
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_every_replica_count(orc, R, path):
-    """R = 1..8 through each store path: the small-batch mapping (300 tokens),
-    the main kernel with streamed whole lines (the same tokens behind padded
+    """R = 1..8 through each store path: the small-batch mapping (300 tokens, and
+    just below its size limit), the main kernel with streamed whole lines (the same tokens behind padded
     ones), with write-back stores (a batch writing about 24 MB) and with
     write-through stores (just over 32 MB).  Whole buffers against the oracle."""
     rng = np.random.default_rng(500 + R)
-    T = {"small": 300, "main": 300, "write_back": (24 << 20) // (R * 788),
+    T = {"small": 300, "small_max": 2047 if R <= 2 else 1023, "main": 300, "write_back": (24 << 20) // (R * 788),
          "write_through": (32 << 20) // (R * 788) + 97}[path]
     num_pages = max(16, 2 * ((T + 63) // 64))
     layout = CacheLayout(replicas=R, layers=1, num_pages=num_pages, guard=64)
