@@ -35,7 +35,9 @@
 //
 // Every piece is stored straight to its slot in each replica; the inputs are
 // read with non-temporal loads (read once, never reused).  How the stores
-// treat the L2 depends on the launch size (see put_at).
+// treat the L2 depends on the launch size (see put_at).  Batches of up to
+// about a thousand tokens take small_store_kernel instead, which spreads a
+// group's five rounds over five waves with the same per-tile arithmetic.
 #include "kvpub_internal.h"
 
 namespace kvpub {

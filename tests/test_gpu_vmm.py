@@ -221,3 +221,46 @@ def test_vmm_broken_storage_fails_closed(monkeypatch):
         kvpub.check(kvpub.kvpub_destroy(ctx))
     finally:
         kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
+
+
+def test_vmm_repeated_growth(orc):
+    """Grow 8 -> 16 -> 40 -> 64 pages (the reserved maximum): after each step the
+    bases are unchanged, every byte written before is still there, and slots of
+    the new pages can be stored."""
+    G.log("vmm: repeated growth, R=2, L=2, 8 -> 16 -> 40 -> 64 pages")
+    t = G.torch()
+    hip = G.hip_runtime()
+    R, L = 2, 2
+    steps = [8, 16, 40, 64]
+    cfg = kvpub.kvpub_config_init(R, L, steps[0])
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, steps[-1])
+    kvpub.check(st, "kvpub_vmm_create")
+    try:
+        fill_pages(hip, cfg, mb, ib, 0, steps[0], L)
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st)
+        mirror = Mirror(cfg, L)
+        rng = np.random.default_rng(54)
+        s = t.cuda.current_stream().cuda_stream
+        prev = 0
+        for i, pages in enumerate(steps):
+            if i:
+                kvpub.check(kvpub.kvpub_vmm_grow(vmm, pages, ctx), "kvpub_vmm_grow")
+                assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, pages)
+                fill_pages(hip, cfg, mb, ib, prev, pages, L)
+            # new rows in the pages this step added, in both layers
+            new = rng.permutation(np.arange(prev * 64, pages * 64))[:200].astype(np.int64)
+            for layer in range(L):
+                x = W.LayerInputs(*W._normal_rows(rng, new.size), new)
+                d = G.DeviceInputs(x)
+                kvpub.check(kvpub.kvpub_store(ctx, layer, d.T, d.latent.data_ptr(), 512, d.rope.data_ptr(), 64,
+                                              d.indexer.data_ptr(), 128, d.slots.data_ptr(), s))
+                t.cuda.synchronize()
+                assert mirror.store(orc, pages, layer, x) == 0
+            compare_backed(hip, cfg, mb, ib, mirror, pages, L, f"after growing to {pages} pages")
+            prev = pages
+        st, invalid, _ = kvpub.kvpub_error_read(ctx, False)
+        assert invalid == 0
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
