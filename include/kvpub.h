@@ -212,13 +212,15 @@ KVPUB_API kvpub_status kvpub_vmm_create(kvpub_config *cfg, uint64_t max_pages, v
  * max_pages; never shrinks).  Bytes already written and all addresses are
  * unchanged.  If ctx is not NULL it must be a context over exactly this
  * storage (same bases and strides, else KVPUB_ERR_INVALID_ARG); its capacity
- * becomes the backed page count for launches made after the call (a graph
- * captured before keeps the capacity it was captured with).  Host-side, not
+ * becomes the backed page count, for launches made after the call and for
+ * graphs captured before it alike (the kernels read the capacity from the
+ * context's device words when they run).  Host-side, not
  * for use during stream capture or concurrently with launches on ctx from
  * another thread.  On failure the page count stays as it was, except in the
  * unlikely case that a layer's old backing could not be restored either:
  * then the storage reports 0 pages, ctx (if given) accepts no slot any more
- * (stores count every slot as invalid, gathers are refused), and
+ * (stores count every slot as invalid, new gathers are refused and gathers
+ * captured earlier write zero rows), and
  * KVPUB_ERR_HIP is returned.  Growing copies each layer's backed bytes
  * once (the addresses stay, the physical memory behind them is replaced). */
 KVPUB_API kvpub_status kvpub_vmm_grow(kvpub_vmm *vmm, uint64_t num_pages, kvpub_ctx *ctx);

@@ -12,9 +12,11 @@
 //   round k = 0..3: token k's latent, lanes 16j..16j+15 = tile j;
 //   round 4:        the indexer rows, lanes 16g..16g+15 = token g;
 // lanes 0..31 also carry the 4 tokens' RoPE rows (8 lanes x 16 B each).
-// The slots arrive through scalar loads.  A padded or out-of-range slot reads
-// slot 0's bytes (always in bounds, so no load sits behind a branch) and its
-// output row is written as zeros.  Decode: the gfx950 OCP e4m3 -> f32 convert
+// The slots and the capacity (from the context's device words, so a captured
+// gather sees a grown storage) arrive through scalar loads.  A padded or
+// out-of-range slot reads slot 0's bytes (always in bounds, so no load sits
+// behind a branch) and its output row is written as zeros; with no backed
+// page at all nothing is read.  Decode: the gfx950 OCP e4m3 -> f32 convert
 // (exact), one binary32 multiply by the tile scale, a round-to-nearest-even
 // f32 -> bf16 convert; each lane stores 8 bf16 = 16 bytes.  Every output line
 // is written whole, so the stores stream past L2 (non-temporal): nothing is
@@ -88,20 +90,38 @@ __device__ __forceinline__ T ld_nt(const uint8_t* p) {
 // SGPRs (kernel-argument preloading): the slot loads issue at once.
 __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
     const int64_t* __restrict__ slots, uint32_t num_tokens, const uint8_t* main_base, const uint8_t* idx_base,
-    uint64_t main_page_stride, uint64_t idx_page_stride, uint64_t capacity, const GatherParams p) {
+    uint64_t main_page_stride, uint64_t idx_page_stride, const CtxHead* __restrict__ head, const GatherParams p) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t num_blocks = (num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock;   // == gridDim.x
     const uint32_t t0 = (xcd_chunk(blockIdx.x, num_blocks) * kGatherWaves + wave) * 4u;
     if (t0 >= num_tokens) return;
     const uint32_t last = num_tokens - 1;
+    const int64_t capacity = head->capacity;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (capacity == 0) {
+        // no page is backed (a VMM storage that lost a layer): read nothing,
+        // every output row is zero and every non-padded slot is counted
+        uint32_t n = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (t0 + k > last) break;
+            n += slots[t0 + k] != -1 ? 1u : 0u;
+            st_nt<u32x4>(p.latent + (uint64_t)(t0 + k) * p.latent_stride + lane * 8u, zero);
+        }
+        const uint32_t g = lane >> 4, r = (lane >> 3) & 3u;
+        if (t0 + g <= last) st_nt<u32x4>(p.indexer + (uint64_t)(t0 + g) * p.indexer_stride + (lane & 15u) * 8u, zero);
+        if (lane < 32u && t0 + r <= last) st_nt<u32x4>(p.rope + (uint64_t)(t0 + r) * p.rope_stride + (lane & 7u) * 8u, zero);
+        if (n != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)n);
+        return;
+    }
     uint64_t row[4], irow[4], iscl[4];
     uint32_t ok = 0, nbad = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint32_t t = t0 + k < last ? t0 + k : last;
         const int64_t v = t0 + k <= last ? slots[t] : -1;
-        const bool good = slot_ok(v, (int64_t)capacity);
+        const bool good = slot_ok(v, capacity);
         nbad += (v != -1 && !good) ? 1u : 0u;
         ok |= good ? (1u << k) : 0u;
         const uint64_t s = good ? (uint64_t)v : 0u;   // bad slots read slot 0 (in bounds) and emit zeros
@@ -132,7 +152,6 @@ __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
     if (nbad != 0 && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
 
     // dequantize and store
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         if (t0 + k > last) break;                // uniform: the tail of the last group
@@ -163,7 +182,7 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
         const uint32_t blocks = (uint32_t)((q.num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock);
         gather_kernel<<<dim3(blocks), dim3(kGatherWaves * 64), 0, stream>>>(
             q.slots, (uint32_t)q.num_tokens, q.main_base, q.idx_base, q.main_page_stride, q.idx_page_stride,
-            (uint64_t)q.capacity, q);
+            q.head, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -3,6 +3,8 @@
 // path; creation is all-or-nothing (vLLM PR #54030 "[Perf][PCP] Fuse
 // direct-KV publication fence", commit list: opt-in allocation either fully
 // succeeds at startup or leaves nothing behind; teardown drops every view).
+#include <algorithm>
+#include <cstddef>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -141,7 +143,6 @@ StoreParams store_params(kvpub_ctx* ctx, uint32_t layer, int64_t T, const void* 
     p.indexer_stride = is;
     p.slots = slots;
     p.num_tokens = T;
-    p.capacity = (int64_t)(ctx->cfg.num_pages * KVPUB_SLOTS_PER_PAGE);
     p.main_page_stride = ctx->cfg.main_page_stride;
     p.idx_page_stride = ctx->cfg.idx_page_stride;
     for (uint32_t r = 0; r < ctx->cfg.num_replicas; ++r) {
@@ -149,10 +150,14 @@ StoreParams store_params(kvpub_ctx* ctx, uint32_t layer, int64_t T, const void* 
         p.idx_base[r] = ctx->idx_base[r] + (uint64_t)layer * ctx->cfg.idx_layer_stride;
     }
     p.invalid_count = reinterpret_cast<unsigned long long*>(ctx->words + kvpub::kInvalidOffset);
-    p.status = reinterpret_cast<const uint32_t*>(ctx->words + kvpub::kStatusOffset);
-    // a layer of one replica in 32-bit offsets (the write-through store path)?
-    const uint64_t main_region = ctx->cfg.num_pages * ctx->cfg.main_page_stride;
-    const uint64_t idx_region = ctx->cfg.num_pages * ctx->cfg.idx_page_stride;
+    p.head = reinterpret_cast<const kvpub::CtxHead*>(ctx->words + kvpub::kStatusOffset);
+    // The write-through store path takes 32-bit offsets within a replica's
+    // layer span: every page the layer may ever hold (a VMM storage's capacity
+    // can grow under a captured graph, so the span, not the current page count).
+    const uint64_t main_region = std::max(ctx->cfg.num_pages * ctx->cfg.main_page_stride,
+                                          ctx->cfg.num_layers > 1 ? ctx->cfg.main_layer_stride : 0);
+    const uint64_t idx_region = std::max(ctx->cfg.num_pages * ctx->cfg.idx_page_stride,
+                                         ctx->cfg.num_layers > 1 ? ctx->cfg.idx_layer_stride : 0);
     if (main_region <= UINT32_MAX && idx_region <= UINT32_MAX) {
         p.main_region = (uint32_t)main_region;
         p.idx_region = (uint32_t)idx_region;
@@ -200,7 +205,14 @@ bool ctx_uses_storage(const kvpub_ctx* ctx, uint32_t replicas, uint8_t* const* m
     return true;
 }
 
-void ctx_set_pages(kvpub_ctx* ctx, uint64_t num_pages) { ctx->cfg.num_pages = num_pages; }
+hipError_t ctx_set_pages(kvpub_ctx* ctx, uint64_t num_pages) {
+    ctx->cfg.num_pages = num_pages;
+    const int64_t capacity = (int64_t)(num_pages * KVPUB_SLOTS_PER_PAGE);
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return hipErrorInvalidDevice;
+    return hipMemcpy(ctx->words + kvpub::kStatusOffset + offsetof(CtxHead, capacity), &capacity, sizeof capacity,
+                     hipMemcpyHostToDevice);
+}
 
 }  // namespace kvpub
 
@@ -262,6 +274,10 @@ KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_b
     hipError_t e = alloc.next_fails() ? hipErrorOutOfMemory : hipMalloc(&c->words, wb);
     if (e != hipSuccess) { c->words = nullptr; release(c); return map_hip(e); }
     e = hipMemset(c->words, 0, wb);
+    if (e != hipSuccess) { release(c); return map_hip(e); }
+    const int64_t capacity = (int64_t)(cfg->num_pages * KVPUB_SLOTS_PER_PAGE);
+    e = hipMemcpy(c->words + kvpub::kStatusOffset + offsetof(kvpub::CtxHead, capacity), &capacity,
+                  sizeof capacity, hipMemcpyHostToDevice);
     if (e != hipSuccess) { release(c); return map_hip(e); }
 
     if (cfg->num_participants > 1) {
@@ -325,7 +341,7 @@ KVPUB_API kvpub_status kvpub_gather(kvpub_ctx* ctx, uint32_t replica, uint32_t l
     g.idx_base = ctx->idx_base[replica] + (uint64_t)layer * ctx->cfg.idx_layer_stride;
     g.main_page_stride = ctx->cfg.main_page_stride;
     g.idx_page_stride = ctx->cfg.idx_page_stride;
-    g.capacity = (int64_t)(ctx->cfg.num_pages * KVPUB_SLOTS_PER_PAGE);
+    g.head = reinterpret_cast<const kvpub::CtxHead*>(ctx->words + kvpub::kStatusOffset);
     g.slots = slot_mapping;
     g.num_tokens = num_tokens;
     g.latent = static_cast<uint16_t*>(latent_out);

@@ -22,10 +22,22 @@ constexpr uint32_t kStatusPoisoned = 0x2u;
 
 // Words of a context that live in device memory, each on its own 128-byte line.
 constexpr size_t kLine = 128;
-constexpr size_t kStatusOffset = 0;
+constexpr size_t kStatusOffset = 0;          // the CtxHead line
 constexpr size_t kInvalidOffset = kLine;
 constexpr size_t kEpochOffset = 2 * kLine;          // + lane * kLine
 constexpr size_t kSignalStride = kLine / 8;         // uint64 words between participant signals
+
+// The first line of a context's device words: the status flags (set by a
+// fence that timed out) and the number of slots per layer that may be written
+// (set by the host at creation and when a VMM storage grows).  Kernels read
+// both with one scalar load at launch time, so a captured graph sees a
+// capacity raised after its capture.
+struct CtxHead {
+    uint32_t status;
+    uint32_t reserved;
+    int64_t capacity;            // num_pages * 64
+};
+static_assert(sizeof(CtxHead) == 16, "one 16-byte scalar load");
 
 struct StoreParams {
     const uint16_t* latent;      // bf16 bit patterns
@@ -36,15 +48,14 @@ struct StoreParams {
     int64_t indexer_stride;
     const int64_t* slots;
     int64_t num_tokens;
-    int64_t capacity;            // num_pages * 64
     uint64_t main_page_stride;   // bytes
     uint64_t idx_page_stride;
     uint8_t* main_base[kMaxReplicas];  // replica r, already offset to the layer
     uint8_t* idx_base[kMaxReplicas];
     unsigned long long* invalid_count;
-    const uint32_t* status;
-    uint32_t main_region;        // bytes of one replica's layer (num_pages * page stride) if below
-    uint32_t idx_region;         // 2^32, else 0: the write-through path needs 32-bit offsets
+    const CtxHead* head;         // status and capacity
+    uint32_t main_region;        // bytes of one replica's layer span (all the pages it may ever hold)
+    uint32_t idx_region;         // if below 2^32, else 0: the write-through path needs 32-bit offsets
 };
 
 struct FenceParams {
@@ -63,7 +74,7 @@ struct GatherParams {
     const uint8_t* idx_base;
     uint64_t main_page_stride;   // bytes
     uint64_t idx_page_stride;
-    int64_t capacity;            // num_pages * 64
+    const CtxHead* head;         // capacity (num_pages * 64)
     const int64_t* slots;
     int64_t num_tokens;
     uint16_t* latent;            // bf16 outputs
@@ -81,8 +92,9 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 bool ctx_uses_storage(const kvpub_ctx* ctx, uint32_t replicas, uint8_t* const* main_bases,
                       uint8_t* const* idx_bases, uint64_t main_layer_stride, uint64_t idx_layer_stride,
                       uint64_t main_page_stride, uint64_t idx_page_stride);
-// Raise (or set) the number of pages per layer that ctx's launches may write.
-void ctx_set_pages(kvpub_ctx* ctx, uint64_t num_pages);
+// Set the number of pages per layer that ctx's launches may write, on the host
+// and in the device capacity word (synchronous copy; no launch on ctx may run).
+hipError_t ctx_set_pages(kvpub_ctx* ctx, uint64_t num_pages);
 // Enqueue one fence kernel on `stream`.
 hipError_t launch_fence(const FenceParams& p, hipStream_t stream);
 

@@ -264,7 +264,7 @@ __device__ __forceinline__ Bases<R> pin_bases(const StoreParams& p) {
 }
 
 __device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2, int64_t s3, bool poisoned,
-                                             uint32_t lane, const StoreParams& p) {
+                                             int64_t capacity, uint32_t lane, const StoreParams& p) {
     const int64_t sl[4] = {s0, s1, s2, s3};
     uint64_t row[4], irow[4], iscl[4];
     uint32_t tok = 0;
@@ -274,7 +274,7 @@ __device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2,
         row[k] = pin_s(page * p.main_page_stride + in * 656u);
         irow[k] = page * p.idx_page_stride + in * 128u;
         iscl[k] = page * p.idx_page_stride + 8192u + in * 4u;
-        tok |= (!poisoned && slot_ok(sl[k], p.capacity)) ? (1u << k) : 0u;
+        tok |= (!poisoned && slot_ok(sl[k], capacity)) ? (1u << k) : 0u;
     }
     const uint32_t g = lane >> 4, r = (lane >> 3) & 3u;
     Dest d;
@@ -434,7 +434,7 @@ template <int R, bool NT, bool WT>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
-    uint32_t indexer_stride, const uint32_t* __restrict__ status, const StoreParams p) {
+    uint32_t indexer_stride, const CtxHead* __restrict__ head, const StoreParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t run_img[kWavesPerBlock][kRunBytes];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -442,26 +442,27 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const uint32_t t0 = (xcd_chunk(blockIdx.x, num_blocks) * kWavesPerBlock + wave) * kTokensPerWave;
     if (t0 >= num_tokens) return;
     const uint32_t last = num_tokens - 1;
-    // Scalar loads (slots, the status word) do not share a counter with the
-    // row loads, so the destinations are worked out before the rows arrive.
+    // Scalar loads (slots, the status word and capacity) do not share a counter
+    // with the row loads, so the destinations are worked out before the rows
+    // arrive.
     int64_t sl[4];
     fetch_slots(slots, t0, last, sl);
-    const uint32_t st = *status;
+    const CtxHead h = *head;
     Group G;
     fetch_rows(latent, rope, indexer, latent_stride, rope_stride, indexer_stride, t0, last, lane, G);
     __builtin_amdgcn_sched_barrier(0);
-    const bool poisoned = (st & kStatusPoisoned) != 0;  // a fence timed out: fail closed
+    const bool poisoned = (h.status & kStatusPoisoned) != 0;  // a fence timed out: fail closed
     // Slots of tokens past the end become -1; invalid slots (neither -1 nor a
     // slot of the cache) are skipped and counted.
     uint32_t nbad = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         sl[k] = t0 + k <= last ? sl[k] : -1;
-        nbad += (sl[k] != -1 && !slot_ok(sl[k], p.capacity)) ? 1u : 0u;
+        nbad += (sl[k] != -1 && !slot_ok(sl[k], h.capacity)) ? 1u : 0u;
     }
     if (nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
     const Bases<R> b = pin_bases<R>(p);
-    const Dest d = destinations(sl[0], sl[1], sl[2], sl[3], poisoned, lane, p);
+    const Dest d = destinations(sl[0], sl[1], sl[2], sl[3], poisoned, h.capacity, lane, p);
     __builtin_amdgcn_sched_barrier(0);
     quantize_store<R, NT, WT>(G, d, b, lane, (lbyte*)&run_img[wave][0], p.main_region, p.idx_region);
 }
@@ -480,14 +481,14 @@ template <int R>
 __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
-    uint32_t indexer_stride, const uint32_t* __restrict__ status, const StoreParams p) {
+    uint32_t indexer_stride, const CtxHead* __restrict__ head, const StoreParams p) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t round = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // 0..4
     const uint32_t t0 = blockIdx.x * kTokensPerWave;
     const uint32_t last = num_tokens - 1;
     int64_t sl[4];
     fetch_slots(slots, t0, last, sl);
-    const uint32_t st = *status;
+    const CtxHead h = *head;
     u32x4 row, rp = u32x4{0u, 0u, 0u, 0u};
     if (round < 4) {
         const uint32_t t = t0 + round < last ? t0 + round : last;
@@ -497,12 +498,12 @@ __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
         const uint32_t ug = t0 + (lane >> 4), tg = ug < last ? ug : last;
         row = ld16(indexer + (uint64_t)tg * indexer_stride + (lane & 15u) * 8u);
     }
-    const bool poisoned = (st & kStatusPoisoned) != 0;
+    const bool poisoned = (h.status & kStatusPoisoned) != 0;
     uint32_t nbad = 0, tok = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         sl[k] = t0 + k <= last ? sl[k] : -1;
-        const bool good = slot_ok(sl[k], p.capacity);
+        const bool good = slot_ok(sl[k], h.capacity);
         nbad += (sl[k] != -1 && !good) ? 1u : 0u;
         tok |= (!poisoned && good) ? (1u << k) : 0u;
     }
@@ -558,7 +559,7 @@ template <bool NT, bool WT>
 static void launch_r(uint32_t num_replicas, dim3 grid, dim3 block, hipStream_t stream, const uint16_t* lat,
                      const uint16_t* rp, const uint16_t* ix, const int64_t* sl, uint32_t n, const StoreParams& p) {
 #define KVPUB_ROW_ARGS lat, rp, ix, sl, n, (uint32_t)p.latent_stride, (uint32_t)p.rope_stride, \
-    (uint32_t)p.indexer_stride, p.status, p
+    (uint32_t)p.indexer_stride, p.head, p
     switch (num_replicas) {
         case 1: store_kernel<1, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
         case 2: store_kernel<2, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
@@ -575,7 +576,7 @@ static void launch_r(uint32_t num_replicas, dim3 grid, dim3 block, hipStream_t s
 static void launch_small(uint32_t num_replicas, uint32_t n, hipStream_t stream, const StoreParams& p) {
     const dim3 grid((n + kTokensPerWave - 1) / kTokensPerWave), block(kSmallWaves * 64);
 #define KVPUB_ROW_ARGS p.latent, p.rope, p.indexer, p.slots, n, (uint32_t)p.latent_stride, \
-    (uint32_t)p.rope_stride, (uint32_t)p.indexer_stride, p.status, p
+    (uint32_t)p.rope_stride, (uint32_t)p.indexer_stride, p.head, p
     switch (num_replicas) {
         case 1: small_store_kernel<1><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
         case 2: small_store_kernel<2><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;

@@ -276,12 +276,14 @@ KVPUB_API kvpub_status kvpub_vmm_grow(kvpub_vmm* v, uint64_t num_pages, kvpub_ct
         (void)hipSetDevice(prev);
         if (v->broken) {
             v->pages = 0;
-            if (ctx) kvpub::ctx_set_pages(ctx, 0);   // every slot is out of range from now on
+            if (ctx) (void)kvpub::ctx_set_pages(ctx, 0);   // every slot is out of range from now on
             return KVPUB_ERR_HIP;
         }
         if (e != hipSuccess) return status_of(e);
     }
-    if (ctx) kvpub::ctx_set_pages(ctx, v->pages);
+    // the context's capacity, on the host and in its device words (which the
+    // kernels of graphs captured earlier read as well)
+    if (ctx && kvpub::ctx_set_pages(ctx, v->pages) != hipSuccess) return KVPUB_ERR_HIP;
     return KVPUB_OK;
 }
 

@@ -264,3 +264,84 @@ def test_vmm_repeated_growth(orc):
         kvpub.check(kvpub.kvpub_destroy(ctx))
     finally:
         kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
+
+
+def test_vmm_graphs_follow_growth(orc):
+    """Graphs captured before growing see the grown capacity: a store + fence
+    graph and a gather graph are captured while 8 of 40 pages are backed; before
+    growing, slots in the other pages are skipped and counted (and gathered as
+    zero rows); after growing to 40 pages the same graphs store and gather them."""
+    G.log("vmm: graphs captured before growing, R=2, L=2, 8 -> 40 pages")
+    t = G.torch()
+    hip = G.hip_runtime()
+    R, L, P0, P1, T = 2, 2, 8, 40, 300
+    cfg = kvpub.kvpub_config_init(R, L, P0)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, P1)
+    kvpub.check(st, "kvpub_vmm_create")
+    graph = None
+    try:
+        fill_pages(hip, cfg, mb, ib, 0, P0, L)
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st)
+        mirror = Mirror(cfg, L)
+        rng = np.random.default_rng(55)
+        slots = rng.permutation(P1 * 64)[:T].astype(np.int64)
+        slots[::29] = -1
+        assert (slots >= P0 * 64).sum() > 200                      # most slots are beyond the backed pages
+        lat = t.empty((L, T, 512), dtype=t.int16, device="cuda")
+        rope = t.empty((L, T, 64), dtype=t.int16, device="cuda")
+        ind = t.empty((L, T, 128), dtype=t.int16, device="cuda")
+        ds = G.to_dev_i64(slots)
+        ios = [kvpub.layer_io(lat[l].data_ptr(), rope[l].data_ptr(), ind[l].data_ptr(), ds.data_ptr(), T, l)
+               for l in range(L)]
+        st, graph = kvpub.kvpub_graph_create(ctx, ios, 0)
+        kvpub.check(st, "kvpub_graph_create")
+        stream = t.cuda.Stream()
+        outs = [t.zeros((T, w), dtype=t.int16, device="cuda") for w in (512, 64, 128)]
+        g_gather = t.cuda.CUDAGraph()
+        with t.cuda.stream(stream):
+            with t.cuda.graph(g_gather, stream=stream):
+                kvpub.check(kvpub.kvpub_gather(ctx, 1, 1, T, ds.data_ptr(), outs[0].data_ptr(), 512,
+                                               outs[1].data_ptr(), 64, outs[2].data_ptr(), 128,
+                                               stream.cuda_stream))
+        t.cuda.synchronize()
+
+        def replay(pages, what):
+            xs = []
+            for l in range(L):
+                x = W.LayerInputs(*W._normal_rows(rng, T), slots)
+                for dst, src in ((lat, x.latent), (rope, x.rope), (ind, x.indexer)):
+                    dst[l].copy_(t.from_numpy(src.view(np.int16)))
+                xs.append(x)
+            t.cuda.synchronize()
+            kvpub.check(kvpub.kvpub_graph_replay(graph, stream.cuda_stream))
+            t.cuda.synchronize()
+            want_invalid = sum(mirror.store(orc, pages, l, xs[l]) for l in range(L))
+            st, invalid, flags = kvpub.kvpub_error_read(ctx, True)
+            kvpub.check(st)
+            assert invalid == want_invalid and flags == 0, (what, invalid, want_invalid)
+            compare_backed(hip, cfg, mb, ib, mirror, pages, L, what)
+            g_gather.replay()
+            t.cuda.synchronize()
+            c = cfg
+            want = orc.gather(mirror.main[1], mirror.idx[1], num_pages=pages, main_page_stride=c.main_page_stride,
+                              main_layer_stride=c.main_layer_stride, idx_page_stride=c.idx_page_stride,
+                              idx_layer_stride=c.idx_layer_stride, layer=1, slot_mapping=slots)
+            for got, w, name in zip(outs, want[:3], ("latent", "rope", "indexer")):
+                assert np.array_equal(got.cpu().numpy().view(np.uint16), w), f"{what}: gathered {name}"
+            kvpub.check(kvpub.kvpub_error_read(ctx, True)[0])
+            return want_invalid
+
+        assert replay(P0, "before growing") > 0
+        kvpub.check(kvpub.kvpub_vmm_grow(vmm, P1, ctx), "kvpub_vmm_grow")
+        fill_pages(hip, cfg, mb, ib, P0, P1, L)
+        assert replay(P1, "after growing") == 0
+        assert kvpub.kvpub_epoch_read(ctx, 0) == (kvpub.KVPUB_OK, 2 * L)
+        del g_gather
+        kvpub.check(kvpub.kvpub_graph_destroy(graph))
+        graph = None
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        if graph is not None:
+            kvpub.kvpub_graph_destroy(graph)
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
