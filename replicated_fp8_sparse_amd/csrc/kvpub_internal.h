@@ -10,10 +10,7 @@ namespace kvpub {
 
 constexpr int kMaxReplicas = 8;
 constexpr int kTokensPerWave = 4;     // 4 tokens x 5 tiles = 5 rounds of 4 tiles per wave
-#ifndef KVPUB_WPB
-#define KVPUB_WPB 4
-#endif
-constexpr int kWavesPerBlock = KVPUB_WPB;     // 256 threads, 16 tokens per block
+constexpr int kWavesPerBlock = 4;     // 256 threads, 16 tokens per block (1, 2 and 8 measured: no better)
 constexpr int kTokensPerBlock = kTokensPerWave * kWavesPerBlock;
 constexpr int64_t kMaxTokensPerLaunch = int64_t(1) << 24;   // larger batches take several launches
 
