@@ -241,3 +241,45 @@ def test_create_rejects_bad_config():
         assert st == kvpub.KVPUB_ERR_INVALID_ARG
     finally:
         dev.free()
+
+
+def test_graph_with_empty_and_mixed_layers(orc):
+    """A captured sequence whose layers hold 0, 5, 300 and 2500 tokens (no store,
+    the small-batch mapping, and the main kernel): every layer still fences once
+    per replay, and the written bytes equal the oracle's after two replays."""
+    import torch
+    layout = CacheLayout(replicas=2, layers=4, num_pages=64, guard=64)
+    sizes = [0, 5, 300, 2500]
+    rng = np.random.default_rng(77)
+    dev = G.DeviceCache(layout)
+    graph = None
+    try:
+        xs, keep = [], []
+        for layer, T in enumerate(sizes):
+            slots = rng.permutation(layout.capacity)[:T].astype(np.int64)
+            if T > 10:
+                slots[::13] = -1
+            xs.append(W.LayerInputs(*W._normal_rows(rng, T), slots))
+        ios = []
+        for layer, x in enumerate(xs):
+            d = G.DeviceInputs(x)
+            keep.append(d)
+            ios.append(kvpub.layer_io(d.latent.data_ptr() if x.slots.size else 0,
+                                      d.rope.data_ptr() if x.slots.size else 0,
+                                      d.indexer.data_ptr() if x.slots.size else 0,
+                                      d.slots.data_ptr() if x.slots.size else 0, x.slots.size, layer))
+        st, graph = kvpub.kvpub_graph_create(dev.ctx, ios, 0)
+        kvpub.check(st, "kvpub_graph_create")
+        s = torch.cuda.current_stream().cuda_stream
+        for _ in range(2):
+            kvpub.check(kvpub.kvpub_graph_replay(graph, s))
+        torch.cuda.synchronize()
+        assert dev.epoch(0) == 2 * len(sizes)
+        mains, idxs, want_invalid = G.oracle_replicas(orc, layout, list(enumerate(xs)))
+        G.assert_full_parity(dev, mains, idxs)
+        st, invalid, flags = dev.errors()
+        assert invalid == 2 * want_invalid and flags == 0
+    finally:
+        if graph is not None:
+            kvpub.kvpub_graph_destroy(graph)
+        dev.free()
