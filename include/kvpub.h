@@ -138,7 +138,8 @@ KVPUB_API void kvpub_config_init(kvpub_config *cfg, uint32_t num_replicas, uint3
  * main_bases[r] / idx_bases[r]: device pointers, 16-byte aligned, each at least
  * (L-1)*layer_stride + num_pages*page_stride bytes.  The caller keeps ownership
  * and must keep them alive until kvpub_destroy.  The context owns only its
- * device words (epochs, participant signals, error counters) on `device`.
+ * device words (status flags and slot capacity, invalid-slot counter, epochs,
+ * participant signals) on `device`.
  * All-or-nothing: on any failure every resource it made is released and *out
  * is set to NULL.  Returns KVPUB_ERR_UNSUPPORTED unless the device is gfx950. */
 KVPUB_API kvpub_status kvpub_create(const kvpub_config *cfg, void *const *main_bases,
