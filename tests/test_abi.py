@@ -98,3 +98,52 @@ def test_product_code_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "kvpub_oracle" not in text and "kvo_" not in text, f
+
+
+def _cfg(**kw):
+    cfg = kvpub.kvpub_config_init(2, 2, 8)
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+@pytest.mark.parametrize("field,value", [
+    ("struct_size", 8),                                  # wrong ABI size
+    ("num_replicas", 0), ("num_replicas", 9),            # R in 1..8
+    ("num_layers", 0),
+    ("block_size", 32),                                  # pages hold 64 slots
+    ("num_pages", 0), ("num_pages", (1 << 40) + 1),
+    ("main_page_stride", 41984 - 16), ("main_page_stride", 41984 + 8),   # >= 64*656, multiple of 16
+    ("idx_page_stride", 8448 - 16), ("idx_page_stride", 8448 + 4),       # >= 64*132, multiple of 16
+    ("main_layer_stride", 8 * 41984 - 16),               # L > 1: room for every page
+    ("idx_layer_stride", 8 * 8448 + 8),                  # L > 1: multiple of 16
+    ("num_lanes", 0), ("num_lanes", 65),
+    ("num_participants", 0), ("num_participants", 9),
+    ("device", -1),
+    ("flags", 1),                                        # reserved
+])
+def test_create_rejects_each_bad_config_field(field, value):
+    """Every configuration rule is checked on the host before any HIP call."""
+    cfg = _cfg(**{field: value})
+    st, ctx = kvpub.kvpub_create(cfg, [16, 32], [16, 32])
+    assert st == kvpub.KVPUB_ERR_INVALID_ARG and ctx is None
+
+
+def test_config_init_defaults():
+    cfg = kvpub.kvpub_config_init(3, 5, 100)
+    assert (cfg.struct_size, cfg.num_replicas, cfg.num_layers, cfg.block_size, cfg.num_pages) == \
+        (ctypes.sizeof(kvpub.kvpub_config), 3, 5, 64, 100)
+    assert (cfg.main_page_stride, cfg.idx_page_stride) == (64 * 656, 64 * 132)
+    assert (cfg.main_layer_stride, cfg.idx_layer_stride) == (100 * 64 * 656, 100 * 64 * 132)
+    assert (cfg.num_lanes, cfg.num_participants, cfg.fence_timeout_ns, cfg.device, cfg.flags) == (1, 1, 0, 0, 0)
+
+
+def test_one_layer_ignores_the_layer_strides():
+    """With L == 1 the layer strides are not used; a config with arbitrary ones
+    gets past validation (and only then needs a device)."""
+    cfg = kvpub.kvpub_config_init(1, 1, 8)
+    cfg.main_layer_stride, cfg.idx_layer_stride = 3, 5
+    st, ctx = kvpub.kvpub_create(cfg, [16], [16])       # no device here: HIP error, else a context
+    assert st != kvpub.KVPUB_ERR_INVALID_ARG
+    if ctx is not None:
+        kvpub.kvpub_destroy(ctx)
