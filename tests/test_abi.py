@@ -147,3 +147,18 @@ def test_one_layer_ignores_the_layer_strides():
     assert st != kvpub.KVPUB_ERR_INVALID_ARG
     if ctx is not None:
         kvpub.kvpub_destroy(ctx)
+
+
+def test_the_abi_from_plain_c(tmp_path):
+    """A C99 program built against include/kvpub.h alone links libkvpub.so and
+    gets the documented host-side answers (no GPU involved)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(kvpub.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-o", exe,
+           os.path.join(root, "tests", "c", "abi_from_c.c"), "-I", os.path.join(root, "include"),
+           "-L", lib_dir, "-lkvpub", f"-Wl,-rpath,{lib_dir}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
