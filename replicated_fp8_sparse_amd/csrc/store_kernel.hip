@@ -60,9 +60,10 @@ constexpr int64_t kWriteThroughBytes = int64_t(32) << 20;           // more than
 constexpr int64_t kSmallBatchTokens = 1024;
 
 // Store policy by launch size:
-//   NT (a launch writing at most kStreamingStoreBytes): whole-line pieces (row
-//     runs, Indexer-K codes) are stored non-temporally, the partial pieces with
-//     ordinary write-back stores.  Nothing of the whole lines is left dirty in
+//   NT (a launch writing at most kStreamingStoreBytes): the pieces made of
+//     whole lines (row runs -- all but one edge line of a 2624-byte run -- and
+//     Indexer-K codes) are stored non-temporally, the partial pieces (scales,
+//     the per-row path) with ordinary write-back stores.  Nothing of the whole lines is left dirty in
 //     L2 for the end-of-kernel write-back, which a latency-bound launch would
 //     otherwise wait for, while the partial lines still merge in L2.
 //   WT (a launch writing more than kWriteThroughBytes, more than the eight
@@ -71,7 +72,7 @@ constexpr int64_t kSmallBatchTokens = 1024;
 //     it, so the writes stream out while the kernel runs instead of being
 //     evicted later.  Buffer offsets are 32-bit, so WT needs each replica's
 //     layer to span less than 2^32 bytes; the buffer's range check
-//     (num_records = the layer's size) drops any store outside the layer.
+//     (num_records = the layer's span) drops any store outside the layer.
 //   otherwise (launches in between, or layers too large for WT): ordinary
 //     write-back stores, which the L2s absorb.
 template <bool NT, class T>
@@ -83,7 +84,7 @@ __device__ __forceinline__ void put(gptr<T> p, T v) {
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data format (gfx950)
 constexpr int kDeviceCoherent = 16;      // buffer cache-policy bits: sc1
 
-// Store v at base + off: `whole` marks a piece that covers whole 128-byte lines.
+// Store v at base + off: `whole` marks a piece of the whole-line kind (see above).
 template <bool NT, bool WT, bool whole, class T>
 __device__ __forceinline__ void put_at(gbyte* base, uint32_t region, uint64_t off, T v) {
     if constexpr (WT) {
@@ -592,8 +593,9 @@ static void launch_small(uint32_t num_replicas, uint32_t n, hipStream_t stream, 
 
 hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream) {
     if (num_replicas < 1 || num_replicas > (uint32_t)kMaxReplicas) return hipErrorInvalidValue;
-    // One wave per group of 4 tokens; batches beyond kMaxTokensPerLaunch are
-    // split so that the grid stays far inside its limits.
+    // Small batches: five waves per group of 4 tokens.  Otherwise one wave per
+    // group, with batches beyond kMaxTokensPerLaunch split so that the grid
+    // stays far inside its limits, and the store policy chosen per launch.
     (void)hipGetLastError();
     if (p.num_tokens <= (num_replicas <= 2 ? 2 * kSmallBatchTokens : kSmallBatchTokens)) {
         launch_small(num_replicas, (uint32_t)p.num_tokens, stream, p);
