@@ -345,3 +345,45 @@ def test_vmm_graphs_follow_growth(orc):
         if graph is not None:
             kvpub.kvpub_graph_destroy(graph)
         kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
+
+
+def test_vmm_gather_graph_replayed_on_broken_storage(monkeypatch):
+    """A gather captured while the storage is fine and replayed after it broke
+    (capacity 0 in the context's device words) reads nothing from the cache:
+    every output row is zero and every non-padded slot is counted."""
+    G.log("vmm: gather graph replayed on a broken storage, R=1, L=1, 8 pages")
+    t = G.torch()
+    cfg = kvpub.kvpub_config_init(1, 1, 8)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, 32)
+    kvpub.check(st, "kvpub_vmm_create")
+    try:
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st)
+        T = 37
+        slots = np.arange(T, dtype=np.int64) * 7
+        slots[::5] = -1
+        ds = G.to_dev_i64(slots)
+        outs = [t.full((T, w), 0x3F80, dtype=t.int16, device="cuda") for w in (512, 64, 128)]
+        stream = t.cuda.Stream()
+        g = t.cuda.CUDAGraph()
+        with t.cuda.stream(stream):
+            with t.cuda.graph(g, stream=stream):
+                kvpub.check(kvpub.kvpub_gather(ctx, 0, 0, T, ds.data_ptr(), outs[0].data_ptr(), 512,
+                                               outs[1].data_ptr(), 64, outs[2].data_ptr(), 128, stream.cuda_stream))
+        t.cuda.synchronize()
+        monkeypatch.setenv("KVPUB_TEST_VMM_GROW_FAIL", "restore")
+        assert kvpub.kvpub_vmm_grow(vmm, 16, ctx) == kvpub.KVPUB_ERR_HIP
+        monkeypatch.delenv("KVPUB_TEST_VMM_GROW_FAIL")
+        assert kvpub.kvpub_vmm_pages(vmm) == (kvpub.KVPUB_OK, 0)
+        kvpub.check(kvpub.kvpub_error_read(ctx, True)[0])
+        g.replay()
+        t.cuda.synchronize()
+        for o in outs:
+            assert not o.any(), "rows gathered from a storage with no backed page must be zero"
+        st, invalid, _ = kvpub.kvpub_error_read(ctx, False)
+        kvpub.check(st)
+        assert invalid == int((slots != -1).sum())
+        del g
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
