@@ -118,15 +118,20 @@ typedef struct {
     uint32_t block_size;        /* slots per page; must be 64 */
     uint64_t num_pages;         /* pages per replica per layer, >= 1 */
     uint64_t main_page_stride;  /* bytes, >= 41984, multiple of 16 */
-    uint64_t main_layer_stride; /* bytes, >= num_pages*main_page_stride, multiple of 16 (ignored if L == 1) */
+    uint64_t main_layer_stride; /* bytes, >= num_pages*main_page_stride, multiple of 16 (L == 1: see below) */
     uint64_t idx_page_stride;   /* bytes, >= 8448, multiple of 16 */
-    uint64_t idx_layer_stride;  /* bytes, >= num_pages*idx_page_stride, multiple of 16 (ignored if L == 1) */
+    uint64_t idx_layer_stride;  /* bytes, >= num_pages*idx_page_stride, multiple of 16 (L == 1: see below) */
     uint32_t num_lanes;         /* fence lanes (one per overlapped micro-batch), 1..64 */
     uint32_t num_participants;  /* fence participants, 1..8; > 1 only with host-driven peers (tests) */
     uint64_t fence_timeout_ns;  /* 0 = 5 s */
     int32_t device;             /* HIP device ordinal */
     uint32_t flags;             /* reserved, must be 0 */
 } kvpub_config;
+/* With L == 1 the layer strides address nothing and are not checked; a value
+ * above num_pages * page stride states the span the layer may grow into
+ * (kvpub_vmm_create sets it to the reserved range), which large stores use as
+ * the bound of their write-through buffer range.  Any value is safe: no store
+ * goes beyond the context's capacity. */
 
 /* Fill *cfg with defaults for R replicas of L layers of num_pages dense pages:
  * page strides 41984 / 8448, layer strides num_pages * page stride, one lane,

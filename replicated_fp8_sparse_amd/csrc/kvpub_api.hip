@@ -154,10 +154,12 @@ StoreParams store_params(kvpub_ctx* ctx, uint32_t layer, int64_t T, const void* 
     // The write-through store path takes 32-bit offsets within a replica's
     // layer span: every page the layer may ever hold (a VMM storage's capacity
     // can grow under a captured graph, so the span, not the current page count).
-    const uint64_t main_region = std::max(ctx->cfg.num_pages * ctx->cfg.main_page_stride,
-                                          ctx->cfg.num_layers > 1 ? ctx->cfg.main_layer_stride : 0);
-    const uint64_t idx_region = std::max(ctx->cfg.num_pages * ctx->cfg.idx_page_stride,
-                                         ctx->cfg.num_layers > 1 ? ctx->cfg.idx_layer_stride : 0);
+    // The layer stride is that span for one layer too: kvpub_vmm_create sets it
+    // to the reserved range whatever the layer count.  Stores never go beyond
+    // the capacity in the context's device words, so a span larger than the
+    // caller's buffer only loosens this second range check.
+    const uint64_t main_region = std::max(ctx->cfg.num_pages * ctx->cfg.main_page_stride, ctx->cfg.main_layer_stride);
+    const uint64_t idx_region = std::max(ctx->cfg.num_pages * ctx->cfg.idx_page_stride, ctx->cfg.idx_layer_stride);
     if (main_region <= UINT32_MAX && idx_region <= UINT32_MAX) {
         p.main_region = (uint32_t)main_region;
         p.idx_region = (uint32_t)idx_region;

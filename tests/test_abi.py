@@ -139,7 +139,7 @@ def test_config_init_defaults():
 
 
 def test_one_layer_ignores_the_layer_strides():
-    """With L == 1 the layer strides are not used; a config with arbitrary ones
+    """With L == 1 the layer strides address nothing and are not checked; a config with arbitrary ones
     gets past validation (and only then needs a device)."""
     cfg = kvpub.kvpub_config_init(1, 1, 8)
     cfg.main_layer_stride, cfg.idx_layer_stride = 3, 5

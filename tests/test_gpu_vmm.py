@@ -387,3 +387,63 @@ def test_vmm_gather_graph_replayed_on_broken_storage(monkeypatch):
         kvpub.check(kvpub.kvpub_destroy(ctx))
     finally:
         kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
+
+
+def test_vmm_one_layer_write_through_graph_follows_growth(orc):
+    """One-layer storage, a launch large enough for the write-through store path
+    (R=4, T=12288: 38.7 MB written), captured before growing: the stores' buffer
+    range covers the layer's whole reserved span, so after growing the same graph
+    writes the new pages (a range sized to the pages backed at capture would drop
+    those stores without a trace)."""
+    G.log("vmm: one layer, write-through launch in a graph captured before growing, R=4, 64 -> 256 pages")
+    t = G.torch()
+    hip = G.hip_runtime()
+    R, L, P0, P1, T = 4, 1, 64, 256, 12288
+    assert T * R * 788 > 32 << 20                                 # takes the write-through path
+    cfg = kvpub.kvpub_config_init(R, L, P0)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, P1)
+    kvpub.check(st, "kvpub_vmm_create")
+    graph = None
+    try:
+        fill_pages(hip, cfg, mb, ib, 0, P0, L)
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st)
+        mirror = Mirror(cfg, L)
+        rng = np.random.default_rng(56)
+        slots = rng.permutation(P1 * 64)[:T].astype(np.int64)
+        assert (slots >= P0 * 64).sum() > T // 2
+        lat = t.empty((T, 512), dtype=t.int16, device="cuda")
+        rope = t.empty((T, 64), dtype=t.int16, device="cuda")
+        ind = t.empty((T, 128), dtype=t.int16, device="cuda")
+        ds = G.to_dev_i64(slots)
+        st, graph = kvpub.kvpub_graph_create(
+            ctx, [kvpub.layer_io(lat.data_ptr(), rope.data_ptr(), ind.data_ptr(), ds.data_ptr(), T, 0)], 0)
+        kvpub.check(st, "kvpub_graph_create")
+        stream = t.cuda.Stream()
+
+        def replay(pages, what):
+            x = W.LayerInputs(*W._normal_rows(rng, T), slots)
+            for dst, src in ((lat, x.latent), (rope, x.rope), (ind, x.indexer)):
+                dst.copy_(t.from_numpy(src.view(np.int16)))
+            t.cuda.synchronize()
+            kvpub.check(kvpub.kvpub_graph_replay(graph, stream.cuda_stream))
+            t.cuda.synchronize()
+            want_invalid = mirror.store(orc, pages, 0, x)
+            st, invalid, flags = kvpub.kvpub_error_read(ctx, True)
+            kvpub.check(st)
+            assert invalid == want_invalid and flags == 0, (what, invalid, want_invalid)
+            compare_backed(hip, cfg, mb, ib, mirror, pages, L, what)
+            return want_invalid
+
+        assert replay(P0, "before growing") > 0
+        kvpub.check(kvpub.kvpub_vmm_grow(vmm, P1, ctx), "kvpub_vmm_grow")
+        fill_pages(hip, cfg, mb, ib, P0, P1, L)
+        assert replay(P1, "after growing") == 0
+        assert kvpub.kvpub_epoch_read(ctx, 0) == (kvpub.KVPUB_OK, 2)
+        kvpub.check(kvpub.kvpub_graph_destroy(graph))
+        graph = None
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        if graph is not None:
+            kvpub.kvpub_graph_destroy(graph)
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
