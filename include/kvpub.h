@@ -104,7 +104,9 @@ typedef enum {
     KVPUB_ERR_UNSUPPORTED = 3,   /* device is not gfx950 */
     KVPUB_ERR_HIP = 4,           /* a HIP runtime call failed */
     KVPUB_ERR_CAPTURING = 5,     /* a synchronizing call while a stream capture is active */
-    KVPUB_ERR_FENCE_TIMEOUT = 6  /* a fence timed out: the context is poisoned */
+    KVPUB_ERR_FENCE_TIMEOUT = 6, /* a fence timed out: the context is poisoned */
+    KVPUB_STATUS_MAX_ENUM = 0x7FFFFFFF /* not a status: makes every non-negative int32 a valid
+                                          kvpub_status value, so a C caller may pass any code */
 } kvpub_status;
 
 /* Sticky device flags reported by kvpub_error_read. */

@@ -493,6 +493,7 @@ KVPUB_API const char* kvpub_strerror(kvpub_status s) {
         case KVPUB_ERR_HIP: return "HIP runtime error";
         case KVPUB_ERR_CAPTURING: return "synchronizing call during stream capture";
         case KVPUB_ERR_FENCE_TIMEOUT: return "fence timed out; context poisoned";
+        case KVPUB_STATUS_MAX_ENUM: break;
     }
     return "unknown status";
 }
