@@ -588,7 +588,21 @@ def cpu_baseline(lat, rope, idx, slots_np, layout, seconds):
                       f"{lm} layers on {cores} threads in {em:.1f} s; single-threaded "
                       f"{l1} layers in {e1:.1f} s",
             "single_thread_value": round(one, 1),
-            "host_cpus": os.cpu_count()}
+            "gbps": round(alg_bytes(many, layout.replicas) / 1e9, 3),
+            "single_thread_gbps": round(alg_bytes(one, layout.replicas) / 1e9, 3),
+            "host_cpus": os.cpu_count(),
+            "cpu_model": host_cpu_model()}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def torch_int16():
