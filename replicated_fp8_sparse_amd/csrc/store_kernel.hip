@@ -139,6 +139,32 @@ __device__ __forceinline__ uint32_t lane_amax_bits(u32x4 d) {
     return (uint32_t)(a.x > a.y ? a.x : a.y);
 }
 
+// Lane 0 of every DPP row (lanes 0, 16, 32, 48).
+constexpr uint64_t kLaneInRowMask = 0x0001000100010001ull;
+
+// a in the lanes of `mask`, b elsewhere (the mask is a constant, so it sits in
+// an SGPR pair and the select is one instruction).
+__device__ __forceinline__ uint32_t select_lane_in_row(uint64_t mask, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(mask));
+    return r;
+}
+
+// Lane I of each DPP row, broadcast to the whole row (row_newbcast:I).
+template <int I>
+__device__ __forceinline__ float bcast_lane(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + I, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float bcast_in_row(float v, int i) {   // i: a constant after unrolling
+    switch (i) {
+        case 0: return bcast_lane<0>(v);
+        case 1: return bcast_lane<1>(v);
+        case 2: return bcast_lane<2>(v);
+        case 3: return bcast_lane<3>(v);
+        default: return bcast_lane<4>(v);
+    }
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -313,24 +339,26 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, co
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
 #pragma unroll
     for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(rows[i]));
-    bool fast = true;
+    // Every lane of row j now holds the amax of all five of the row's tiles, so
+    // lane 16j + i takes tile (round i, row j) and one scale sequence covers
+    // the group's 20 tiles (lanes 16j + 5.. repeat round 0's tile).
+    uint32_t mine = ab[0];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        const uint32_t E = ab[i] >> 7;
-        fast = fast && E >= kFastMinExponent && E < 255u;
-    }
+    for (int i = 1; i < 5; ++i) mine = select_lane_in_row(kLaneInRowMask << i, ab[i], mine);
+    const uint32_t E = mine >> 7;
     u32x2 codes[5];
     float scale[5];
-    if (__all(fast)) {
+    if (__all(E >= kFastMinExponent && E < 255u)) {
+        const TileScale t = tile_scale(mine);
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
-            const TileScale t = tile_scale(ab[i]);
+            const float si = bcast_in_row(t.s, i), yi = bcast_in_row(t.y, i);
             float x[8], q[8];
             unpack8(rows[i], x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], t.s, t.y);
+            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], si, yi);
             codes[i] = cvt8(q);
-            scale[i] = t.s;
+            scale[i] = si;
         }
     } else {
         // some tile of the wave has a tiny (possibly subnormal) scale or is all
