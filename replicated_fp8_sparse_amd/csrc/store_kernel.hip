@@ -20,10 +20,13 @@
 // or on the slot values; the slots arrive through scalar loads and every
 // store address is worked out while the rows are in flight.
 //
-// Per tile: amax = the largest magnitude (max3 in-lane, then a 4-step DPP
-// max within the row), scale = RN32(amax / 448), and per element code =
-// e4m3fn(RN32(x / scale)).  The scale and its reciprocal y = RN32(1/scale)
-// come from a short exact sequence (tile_scale); RN32(x/scale) is computed as
+// Per tile: amax = the largest magnitude (packed 16-bit maxima in-lane, then
+// a 4-step DPP max within the row), scale = RN32(amax / 448), and per element
+// code = e4m3fn(RN32(x / scale)).  The scale and its reciprocal y =
+// RN32(1/scale) come from a short exact sequence (tile_scale), run once for a
+// group's 20 tiles: each lane of a DPP row takes one of the row's five tiles,
+// and row_newbcast hands each round's values back to the row.  RN32(x/scale)
+// is computed as
 // q = x*y, t = fma(q, scale, -x), q' = fma(-t, y, q), which is the magnitude
 // form fma(fma(-|x|y, scale, |x|), y, |x|y) with the sign of x put back.
 // For every scale >= 2^-64 this gives the same e4m3 code as a correctly
