@@ -156,7 +156,8 @@ __device__ __forceinline__ uint32_t select_lane_in_row(uint64_t mask, uint32_t a
 // Lane I of each DPP row, broadcast to the whole row (row_newbcast:I).
 template <int I>
 __device__ __forceinline__ float bcast_lane(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + I, 0xF, 0xF, false));
+    // every lane reads a valid source lane: a plain DPP move (no old value to keep)
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + I, 0xF, 0xF, false));
 }
 __device__ __forceinline__ float bcast_in_row(float v, int i) {   // i: a constant after unrolling
     switch (i) {
@@ -166,6 +167,21 @@ __device__ __forceinline__ float bcast_in_row(float v, int i) {   // i: a consta
         case 3: return bcast_lane<3>(v);
         default: return bcast_lane<4>(v);
     }
+}
+
+// Largest magnitude of 8 finite values (exact: a maximum rounds nothing).
+// max3 with absolute-value source modifiers; written out so that no NaN
+// quieting is added around it (the inputs are finite bf16 values).
+__device__ __forceinline__ float max3_abs(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float lane_amax_f32(const float (&x)[8]) {
+    float m = max3_abs(x[0], x[1], x[2]);
+    m = max3_abs(m, x[3], x[4]);
+    m = max3_abs(m, x[5], x[6]);
+    return max3_abs(m, x[7], x[7]);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -218,9 +234,13 @@ __device__ __forceinline__ float quotient_exact(float x, float scale) {
 }
 
 __device__ __forceinline__ u32x2 cvt8(const float (&q)[8]) {
-    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    // The convert writes one 16-bit half and keeps the other from its old
+    // operand; the second convert of each word overwrites the half the first
+    // one kept, so the first one's old operand is any value: its first input,
+    // which dies there, so the result can take its register.
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], __float_as_int(q[0]), false);
     w0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], w0, true);
-    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], 0, false);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[4], q[5], __float_as_int(q[4]), false);
     w1 = __builtin_amdgcn_cvt_pk_fp8_f32(q[6], q[7], w1, true);
     return u32x2{(uint32_t)w0, (uint32_t)w1};
 }
@@ -340,8 +360,22 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, co
                                                lbyte* img, uint32_t main_region, uint32_t idx_region) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
+    if constexpr (NT) {
+        // Launches of this size hold few waves per SIMD, so the unpacked values
+        // may stay live from here to the quotients: the in-lane maximum comes
+        // from them (three max3 of magnitudes instead of eight packed steps).
 #pragma unroll
-    for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(rows[i]));
+        for (int i = 0; i < 5; ++i) {
+            float x[8];
+            unpack8(rows[i], x);
+            // the shift (an ordinary instruction) also stands between the asm
+            // result and the DPP reads, whose wait states are the compiler's
+            ab[i] = row_max16(__float_as_uint(lane_amax_f32(x)) >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(rows[i]));
+    }
     // Every lane of row j now holds the amax of all five of the row's tiles, so
     // lane 16j + i takes tile (round i, row j) and one scale sequence covers
     // the group's 20 tiles (lanes 16j + 5.. repeat round 0's tile).
