@@ -141,6 +141,38 @@ def test_hand_cases_parity(orc, mapping):
     run_full(orc, layout, [(1, x)], f"hand cases T={T} ({mapping} mapping)")
 
 
+@pytest.mark.parametrize("path", ["small", "main", "write_through"])
+def test_skipped_tokens_with_non_finite_rows(orc, path):
+    """Padded and invalid tokens may carry anything in their rows (NaN, infinities,
+    the largest values): the kernels load those rows with their group but no byte
+    they store depends on them.  Skipped tokens are interleaved with valid ones so
+    that they share groups (waves) and tiles' neighbours; the oracle never reads
+    their rows."""
+    rng = np.random.default_rng(202)
+    R, T = (4, 11000) if path == "write_through" else (2, 300 if path == "small" else 2300)
+    skipped = np.zeros(T, bool)
+    skipped[rng.choice(T, T // 3, replace=False)] = True
+    skipped[1::7] = True
+    nvalid = int((~skipped).sum())
+    layout = CacheLayout(replicas=R, layers=1, num_pages=(nvalid + 63) // 64 + 3)
+    latent = bf16_bits(rng.standard_normal((T, 512)).astype(np.float32))
+    rope = rng.integers(0, 65536, size=(T, 64), dtype=np.uint16)
+    indexer = bf16_bits(rng.standard_normal((T, 128)).astype(np.float32))
+    bad = np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x7FA0, 0x7F7F, 0xFF7F], np.uint16)
+    ns = int(skipped.sum())
+    latent[skipped] = rng.choice(bad, size=(ns, 512))
+    indexer[skipped] = rng.choice(bad, size=(ns, 128))
+    latent[skipped, ::5] = 0x7FC0                     # a NaN in every tile of every skipped row
+    slots = np.full(T, -1, np.int64)
+    slots[~skipped] = rng.permutation(layout.capacity)[:nvalid]
+    inval = np.flatnonzero(skipped)[::4]              # a quarter of the skipped tokens: invalid slots
+    slots[inval] = layout.capacity + rng.integers(0, 1000, inval.size)
+    x = LayerInputs(latent, rope, indexer, slots)
+    written = T * R * 788
+    assert (T <= 2048) == (path == "small") and (written > 32 << 20) == (path == "write_through")
+    run_full(orc, layout, [(0, x)], f"non-finite skipped rows, T={T}, R={R} ({path})")
+
+
 @pytest.mark.parametrize("mapping", MAPPINGS)
 def test_encoder_sweep_parity(orc, mapping):
     """Tiles with amax 448 have scale 1.0, so every bf16 value in [-448, 448] is
