@@ -13,7 +13,7 @@
 //   round 4:        the indexer rows, lanes 16g..16g+15 = token g;
 // lanes 0..31 also carry the 4 tokens' RoPE rows (8 lanes x 16 B each).
 // The slots and the capacity (from the context's device words, so a captured
-// gather sees a grown storage) arrive through scalar loads.  A padded or
+// gather sees a grown storage) arrive together through scalar loads.  A padded or
 // out-of-range slot reads slot 0's bytes (always in bounds, so no load sits
 // behind a branch) and its output row is written as zeros; with no backed
 // page at all nothing is read.  Decode: the gfx950 OCP e4m3 -> f32 convert
@@ -88,6 +88,10 @@ __device__ __forceinline__ T ld_nt(const uint8_t* p) {
 
 // The arguments the first instructions need are plain scalars, preloaded in
 // SGPRs (kernel-argument preloading): the slot loads issue at once.
+// Off32: the layer spans less than 2^32 bytes, so the page offsets are 32-bit
+// products (one scalar multiply each instead of a 64-bit sequence): the row
+// loads wait on these, so they sit on the critical path.
+template <bool Off32>
 __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
     const int64_t* __restrict__ slots, uint32_t num_tokens, const uint8_t* main_base, const uint8_t* idx_base,
     uint64_t main_page_stride, uint64_t idx_page_stride, const CtxHead* __restrict__ head, const GatherParams p) {
@@ -97,6 +101,12 @@ __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
     const uint32_t t0 = (xcd_chunk(blockIdx.x, num_blocks) * kGatherWaves + wave) * 4u;
     if (t0 >= num_tokens) return;
     const uint32_t last = num_tokens - 1;
+    // The four slots (token indices clamped to the last token: always in
+    // bounds) and the capacity are fetched together, so a single scalar round
+    // trip precedes the row loads; nothing waits on one before issuing another.
+    int64_t sl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sl[k] = slots[t0 + k < last ? t0 + k : last];
     const int64_t capacity = head->capacity;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     if (capacity == 0) {
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (t0 + k > last) break;
-            n += slots[t0 + k] != -1 ? 1u : 0u;
+            n += sl[k] != -1 ? 1u : 0u;
             st_nt<u32x4>(p.latent + (uint64_t)(t0 + k) * p.latent_stride + lane * 8u, zero);
         }
         const uint32_t g = lane >> 4, r = (lane >> 3) & 3u;
@@ -119,16 +129,23 @@ __global__ __launch_bounds__(kGatherWaves * 64) void gather_kernel(
     uint32_t ok = 0, nbad = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t t = t0 + k < last ? t0 + k : last;
-        const int64_t v = t0 + k <= last ? slots[t] : -1;
+        const int64_t v = t0 + k <= last ? sl[k] : -1;
         const bool good = slot_ok(v, capacity);
         nbad += (v != -1 && !good) ? 1u : 0u;
         ok |= good ? (1u << k) : 0u;
         const uint64_t s = good ? (uint64_t)v : 0u;   // bad slots read slot 0 (in bounds) and emit zeros
         const uint64_t page = s >> 6, in = s & 63u;
-        row[k] = page * main_page_stride + in * 656u;
-        irow[k] = page * idx_page_stride + in * 128u;
-        iscl[k] = page * idx_page_stride + 8192u + in * 4u;
+        if constexpr (Off32) {
+            const uint32_t pg = (uint32_t)page, o = (uint32_t)in;
+            const uint32_t ib = pg * (uint32_t)idx_page_stride;
+            row[k] = pg * (uint32_t)main_page_stride + o * 656u;
+            irow[k] = ib + o * 128u;
+            iscl[k] = ib + 8192u + o * 4u;
+        } else {
+            row[k] = page * main_page_stride + in * 656u;
+            irow[k] = page * idx_page_stride + in * 128u;
+            iscl[k] = page * idx_page_stride + 8192u + in * 4u;
+        }
     }
     ok = __builtin_amdgcn_readfirstlane(ok);
 
@@ -180,9 +197,14 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t stream) {
         q.rope = p.rope + t * p.rope_stride;
         q.indexer = p.indexer + t * p.indexer_stride;
         const uint32_t blocks = (uint32_t)((q.num_tokens + kGatherTokensPerBlock - 1) / kGatherTokensPerBlock);
-        gather_kernel<<<dim3(blocks), dim3(kGatherWaves * 64), 0, stream>>>(
-            q.slots, (uint32_t)q.num_tokens, q.main_base, q.idx_base, q.main_page_stride, q.idx_page_stride,
-            q.head, q);
+        if (q.offsets32)
+            gather_kernel<true><<<dim3(blocks), dim3(kGatherWaves * 64), 0, stream>>>(
+                q.slots, (uint32_t)q.num_tokens, q.main_base, q.idx_base, q.main_page_stride, q.idx_page_stride,
+                q.head, q);
+        else
+            gather_kernel<false><<<dim3(blocks), dim3(kGatherWaves * 64), 0, stream>>>(
+                q.slots, (uint32_t)q.num_tokens, q.main_base, q.idx_base, q.main_page_stride, q.idx_page_stride,
+                q.head, q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

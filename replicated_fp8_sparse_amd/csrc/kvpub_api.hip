@@ -353,6 +353,11 @@ KVPUB_API kvpub_status kvpub_gather(kvpub_ctx* ctx, uint32_t replica, uint32_t l
     g.rope_stride = rope_row_stride;
     g.indexer_stride = indexer_row_stride;
     g.invalid_count = reinterpret_cast<unsigned long long*>(ctx->words + kvpub::kInvalidOffset);
+    // every page the layer may ever hold (as for the store's buffer range):
+    // 32-bit offsets if that span stays below 2^32 bytes
+    const uint64_t main_span = std::max(ctx->cfg.num_pages * ctx->cfg.main_page_stride, ctx->cfg.main_layer_stride);
+    const uint64_t idx_span = std::max(ctx->cfg.num_pages * ctx->cfg.idx_page_stride, ctx->cfg.idx_layer_stride);
+    g.offsets32 = main_span <= UINT32_MAX && idx_span <= UINT32_MAX ? 1u : 0u;
     return map_hip(kvpub::launch_gather(g, static_cast<hipStream_t>(stream)));
 }
 

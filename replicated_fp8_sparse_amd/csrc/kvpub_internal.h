@@ -81,6 +81,7 @@ struct GatherParams {
     int64_t rope_stride;
     int64_t indexer_stride;
     unsigned long long* invalid_count;
+    uint32_t offsets32;          // every offset within a layer fits in 32 bits (layer span < 2^32)
 };
 
 // Enqueue the dequantizing gather on `stream`; returns the launch status.
