@@ -13,8 +13,9 @@
 //   e = epoch[lane] + 1, by an acquire-release RMW at system scope: every
 //       write this GPU made before the fence is visible before the epoch
 //       moves, and what was published before it is visible after;
-//   signal[self] = e (a release store when there are peers to see it);
-//   for every other participant q: acquire-load signal[q] until it is >= e.
+//   with peers only: signal[self] = e (a release store), then for every
+//       other participant q: acquire-load signal[q] until it is >= e.
+// Alone (one participant) the RMW is the whole fence.
 // This GPU's own signal is never awaited: it was written just before, in
 // program order, by the same wave.  The expected value e is read from device
 // memory, never passed as a kernel argument, so replaying a captured launch
@@ -33,15 +34,19 @@ __global__ __launch_bounds__(64) void fence_kernel(uint64_t* epoch, uint64_t* si
                                                    uint32_t num_participants, uint32_t self,
                                                    uint64_t timeout_ticks) {
     if (threadIdx.x != 0) return;
+    if (num_participants == 1) {
+        // Alone, the epoch is the whole barrier: the acquire-release RMW
+        // publishes this GPU's writes and acquires what was published before.
+        // Only a fence waiting for peers can time out and poison the context,
+        // so there is no status to check first (one memory round trip, not two)
+        // and no signal for anyone to read.
+        __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM);
+        return;
+    }
     if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusPoisoned) return;
     const uint64_t e =
         __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM) + 1;
     uint64_t* own = signals + (size_t)self * kSignalStride;
-    if (num_participants == 1) {
-        // no peer reads it: the RMW above already released and acquired
-        __hip_atomic_store(own, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        return;
-    }
     __hip_atomic_store(own, e, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     const uint64_t start = wall_clock64();
     for (uint32_t q = 0; q < num_participants; ++q) {

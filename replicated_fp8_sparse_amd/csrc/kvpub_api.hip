@@ -19,7 +19,7 @@ struct kvpub_ctx {
     kvpub_config cfg;
     uint8_t* main_base[KVPUB_MAX_REPLICAS];
     uint8_t* idx_base[KVPUB_MAX_REPLICAS];
-    uint8_t* words;            // device: status, invalid count, epochs, (P == 1) signals
+    uint8_t* words;            // device: status, invalid count, epochs
     uint64_t* host_signals;    // P > 1: host-coherent signals [lanes][P] (kSignalStride apart)
     uint64_t* host_signals_dev;
     uint64_t timeout_ticks;
@@ -37,20 +37,17 @@ namespace {
 constexpr uint64_t kDefaultTimeoutNs = 5000000000ull;
 
 size_t words_bytes(const kvpub_config& c) {
-    size_t b = kvpub::kEpochOffset + (size_t)c.num_lanes * kvpub::kLine;
-    if (c.num_participants == 1) b += (size_t)c.num_lanes * kvpub::kLine;
-    return b;
+    return kvpub::kEpochOffset + (size_t)c.num_lanes * kvpub::kLine;
 }
 
 uint64_t* epoch_ptr(kvpub_ctx* c, uint32_t lane) {
     return reinterpret_cast<uint64_t*>(c->words + kvpub::kEpochOffset + (size_t)lane * kvpub::kLine);
 }
 
+// Participant signals exist only with peers; alone, the epoch is the barrier.
 uint64_t* signals_dev_ptr(kvpub_ctx* c, uint32_t lane) {
     const uint32_t P = c->cfg.num_participants;
-    if (P == 1)
-        return reinterpret_cast<uint64_t*>(c->words + kvpub::kEpochOffset +
-                                           (size_t)(c->cfg.num_lanes + lane) * kvpub::kLine);
+    if (P == 1) return nullptr;
     return c->host_signals_dev + (size_t)lane * P * kvpub::kSignalStride;
 }
 

@@ -57,7 +57,7 @@ struct StoreParams {
 
 struct FenceParams {
     uint64_t* epoch;             // this lane's epoch word
-    uint64_t* signals;           // this lane's participant signals, kSignalStride apart
+    uint64_t* signals;           // this lane's participant signals, kSignalStride apart (null alone)
     uint32_t num_participants;
     uint32_t self;               // this GPU's participant index (0)
     uint32_t* status;
