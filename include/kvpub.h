@@ -241,14 +241,16 @@ KVPUB_API kvpub_status kvpub_vmm_pages(kvpub_vmm *vmm, uint64_t *num_pages);
 KVPUB_API kvpub_status kvpub_vmm_destroy(kvpub_vmm *vmm);
 
 /* One fence on `lane`, asynchronously on `stream`: a single one-wavefront
- * kernel that adds 1 to the lane's device epoch with a system-scope release,
- * publishes the new value as this participant's signal, and acquire-waits
- * until every participant's signal has reached it.  The expected value is
- * never a kernel argument, so a captured fence advances the epoch on every
- * replay.  If the wait exceeds fence_timeout_ns the kernel records
- * KVPUB_FLAG_FENCE_TIMEOUT | KVPUB_FLAG_POISONED and returns; from then on
- * stores and fences of this context write nothing (fail-closed).  No
- * allocation and no synchronization: safe under stream capture. */
+ * kernel that adds 1 to the lane's device epoch with a system-scope
+ * acquire-release read-modify-write.  With one participant that is the whole
+ * fence.  With peers it then publishes the new value as this participant's
+ * signal and acquire-waits until every other participant's signal has
+ * reached it.  The expected value is never a kernel argument, so a captured
+ * fence advances the epoch on every replay.  If the wait exceeds
+ * fence_timeout_ns the kernel records KVPUB_FLAG_FENCE_TIMEOUT |
+ * KVPUB_FLAG_POISONED and returns; from then on stores and fences of this
+ * context write nothing (fail-closed; only a fence with peers can time out).
+ * No allocation and no synchronization: safe under stream capture. */
 KVPUB_API kvpub_status kvpub_fence(kvpub_ctx *ctx, uint32_t lane, kvpub_stream_t stream);
 
 /* One layer of a captured sequence. */
