@@ -283,3 +283,53 @@ def test_graph_with_empty_and_mixed_layers(orc):
         if graph is not None:
             kvpub.kvpub_graph_destroy(graph)
         dev.free()
+
+
+def test_two_lanes_two_graphs_replayed_concurrently(orc):
+    """Two overlapped micro-batches (one fence lane each): graph A stores 3000
+    tokens per layer (main kernel) and fences lane 0, graph B stores 500 other
+    tokens per layer (small-batch kernel) into the same layers and fences lane 1;
+    they are replayed five times each, concurrently on two streams.  Every byte
+    of every replica equals the oracle applying both micro-batches (their slots
+    are disjoint, so the order between them does not matter), and each lane's
+    epoch counts exactly its own fences."""
+    import torch
+    L, TA, TB, reps = 4, 3000, 500, 5
+    layout = CacheLayout(replicas=2, layers=L, num_pages=64)
+    rng = np.random.default_rng(404)
+    G.log(f"two lanes: graphs of {L} x (store, fence), T={TA} on lane 0 and T={TB} on lane 1, {reps} concurrent replays")
+    dev = G.DeviceCache(layout, lanes=2)
+    graphs = []
+    try:
+        perm = rng.permutation(layout.capacity)
+        sa = perm[:TA].astype(np.int64)
+        sb = perm[TA:TA + TB].astype(np.int64)
+        sa[::97] = -1
+        sb[::31] = -1
+        xa = [W.LayerInputs(*W._normal_rows(rng, TA), sa) for _ in range(L)]
+        xb = [W.LayerInputs(*W._normal_rows(rng, TB), sb) for _ in range(L)]
+        da = [G.DeviceInputs(x) for x in xa]
+        db = [G.DeviceInputs(x) for x in xb]
+        for lane, ds in ((0, da), (1, db)):
+            ios = [kvpub.layer_io(d.latent.data_ptr(), d.rope.data_ptr(), d.indexer.data_ptr(),
+                                  d.slots.data_ptr(), d.T, l) for l, d in enumerate(ds)]
+            st, g = kvpub.kvpub_graph_create(dev.ctx, ios, lane)
+            kvpub.check(st, "kvpub_graph_create")
+            graphs.append(g)
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+        for _ in range(reps):
+            kvpub.check(kvpub.kvpub_graph_replay(graphs[0], s0.cuda_stream), "replay A")
+            kvpub.check(kvpub.kvpub_graph_replay(graphs[1], s1.cuda_stream), "replay B")
+        torch.cuda.synchronize()
+        assert (dev.epoch(0), dev.epoch(1)) == (reps * L, reps * L)
+        st, invalid, flags = dev.errors()
+        assert st == kvpub.KVPUB_OK and invalid == 0 and flags == 0
+        mains, idxs, want_invalid = G.oracle_replicas(orc, layout, [(l, x) for l, x in enumerate(xa)] +
+                                                      [(l, x) for l, x in enumerate(xb)])
+        assert want_invalid == 0
+        G.assert_full_parity(dev, mains, idxs)
+    finally:
+        for g in graphs:
+            kvpub.kvpub_graph_destroy(g)
+        dev.free()
