@@ -333,3 +333,61 @@ def test_two_lanes_two_graphs_replayed_concurrently(orc):
         for g in graphs:
             kvpub.kvpub_graph_destroy(g)
         dev.free()
+
+
+def test_graph_replays_wait_for_a_host_peer_at_each_epoch(orc):
+    """Two participants under graph replay: 4 x (store, fence) captured once and
+    replayed 3 times; a host thread stands in for the peer and publishes epochs
+    1..12 one at a time, 3 ms apart.  Each replayed fence waits for the peer's
+    signal to reach the epoch it has just advanced to (read from the device, not
+    fixed at capture), so the replays can finish only after the last
+    publication -- with an expected value frozen at capture, replays 2 and 3
+    would pass as soon as the peer had published 4.  The epoch ends at 12, no
+    timeout is recorded, and the stored bytes equal the oracle's."""
+    import torch
+    L, reps, gap = 4, 3, 0.003
+    layout = CacheLayout(replicas=2, layers=L, num_pages=8)
+    rng = np.random.default_rng(505)
+    G.log(f"host peer under graph replay: {L} x (store, fence), {reps} replays, peer publishes 1..{L * reps}")
+    dev = G.DeviceCache(layout, participants=2, timeout_ns=10_000_000_000)
+    graph = None
+    try:
+        xs = [W.LayerInputs(*W._normal_rows(rng, 32), rng.permutation(layout.capacity)[:32].astype(np.int64))
+              for _ in range(L)]
+        ds = [G.DeviceInputs(x) for x in xs]
+        ios = [kvpub.layer_io(d.latent.data_ptr(), d.rope.data_ptr(), d.indexer.data_ptr(), d.slots.data_ptr(),
+                              d.T, l) for l, d in enumerate(ds)]
+        st, graph = kvpub.kvpub_graph_create(dev.ctx, ios, 0)
+        kvpub.check(st, "kvpub_graph_create")
+        st, sig = kvpub.kvpub_participant_signal(dev.ctx, 0, 1)
+        kvpub.check(st)
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        published = []
+
+        def peer():
+            for k in range(1, L * reps + 1):
+                time.sleep(gap)
+                published.append(time.perf_counter())   # before the write the GPU may act on
+                sig[0] = k
+
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            kvpub.check(kvpub.kvpub_graph_replay(graph, stream.cuda_stream), "kvpub_graph_replay")
+        th = threading.Thread(target=peer)
+        th.start()
+        stream.synchronize()
+        done = time.perf_counter()
+        th.join()
+        assert len(published) == L * reps
+        assert done >= published[-1], "the replays finished before the peer published the last epoch"
+        assert done - t0 >= (L * reps - 1) * gap
+        assert dev.epoch(0) == L * reps
+        st, invalid, flags = dev.errors()
+        assert st == kvpub.KVPUB_OK and invalid == 0 and flags == 0
+        mains, idxs, _ = G.oracle_replicas(orc, layout, list(enumerate(xs)))
+        G.assert_full_parity(dev, mains, idxs)
+    finally:
+        if graph is not None:
+            kvpub.kvpub_graph_destroy(graph)
+        dev.free()
