@@ -574,6 +574,25 @@ __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
         tok |= (!poisoned && good) ? (1u << k) : 0u;
     }
     if (round == 0 && nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
+    // Store offsets and replica bases (kernel arguments), worked out while the
+    // rows are in flight: fetched after the data they would add a round trip.
+    // Waves 0..3: the token's Main-KV row (uniform); wave 4: this lane's
+    // token's Indexer-K codes and scale.  Offsets of skipped slots are unused.
+    const Bases<R> b = pin_bases<R>(p);
+    uint64_t off0, off1 = 0;
+    if (round < 4) {
+        const uint64_t s = (uint64_t)(round == 0 ? sl[0] : round == 1 ? sl[1] : round == 2 ? sl[2] : sl[3]);
+        off0 = (s >> 6) * p.main_page_stride + (s & 63u) * 656u;
+    } else {
+        const uint32_t g = lane >> 4;
+        const uint64_t s = (uint64_t)(g == 0 ? sl[0] : g == 1 ? sl[1] : g == 2 ? sl[2] : sl[3]);
+        const uint64_t page = (s >> 6) * p.idx_page_stride, in = s & 63u;
+        off0 = page + in * 128u;
+        off1 = page + 8192u + in * 4u;
+    }
+    off0 = pin_v(off0);
+    off1 = pin_v(off1);
+    __builtin_amdgcn_sched_barrier(0);
 
     const uint32_t ab = row_max16(lane_amax_bits(row));
     const uint32_t E = ab >> 7;
@@ -596,25 +615,19 @@ __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
 
     if (round < 4) {
         if (!((tok >> round) & 1u)) return;
-        const uint64_t s = (uint64_t)sl[round];
-        const uint64_t off = (s >> 6) * p.main_page_stride + (s & 63u) * 656u;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            gbyte* rw = (gbyte*)p.main_base[r] + off;
+            gbyte* rw = b.main[r] + off0;
             *(gptr<u32x2>)(rw + lane * 8u) = codes;
             *(gptr<uint32_t>)(rw + 512u + (lane >> 4) * 4u) = __float_as_uint(scale);
             if (lane < 8u) *(gptr<u32x4>)(rw + 528u + lane * 16u) = rp;
         }
     } else {
-        const uint32_t g = lane >> 4;
-        if (!((tok >> g) & 1u)) return;
-        const uint64_t s = (uint64_t)(g == 0 ? sl[0] : g == 1 ? sl[1] : g == 2 ? sl[2] : sl[3]);
-        const uint64_t page = (s >> 6) * p.idx_page_stride, in = s & 63u;
+        if (!((tok >> (lane >> 4)) & 1u)) return;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            gbyte* ib = (gbyte*)p.idx_base[r] + page;
-            *(gptr<u32x2>)(ib + in * 128u + (lane & 15u) * 8u) = codes;
-            *(gptr<uint32_t>)(ib + 8192u + in * 4u) = __float_as_uint(scale);
+            *(gptr<u32x2>)(b.idx[r] + off0 + (lane & 15u) * 8u) = codes;
+            *(gptr<uint32_t>)(b.idx[r] + off1) = __float_as_uint(scale);
         }
     }
 }
