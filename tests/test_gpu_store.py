@@ -473,3 +473,75 @@ def test_every_replica_count(orc, R, path):
     if path == "main":
         x = with_pads(x, MAIN_KERNEL_PADS, rng)
     run_full(orc, layout, [(0, x)], f"R={R} {path} T={x.slots.size}")
+
+
+def _random_rows(rng, T, width):
+    """bf16 rows from a mix of distributions, chosen per token: normal, heavy-tailed
+    with a wide per-token magnitude, all zero, subnormal-only, or with one large
+    element per row."""
+    kind = rng.integers(0, 5, size=T)
+    x = rng.standard_normal((T, width))
+    heavy = kind == 1
+    x[heavy] = (rng.standard_t(3, size=(int(heavy.sum()), width)) *
+                np.exp(rng.normal(0, 3, size=(int(heavy.sum()), 1))))
+    x[kind == 2] = 0.0
+    sub = kind == 3
+    x[sub] = rng.standard_normal((int(sub.sum()), width)) * 1e-39
+    big = np.flatnonzero(kind == 4)
+    x[big, rng.integers(0, width, size=big.size)] *= 1e4
+    x = np.clip(x, -3.0e38, 3.0e38)
+    return bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configurations(orc, seed):
+    """Seeded random configurations, whole buffers against the oracle: replica
+    count, layer count, pages, guard bytes after each page (page strides above
+    the page size), input row strides wider than the rows, the layer stored, a
+    token count spanning both store mappings, and slots mixing distinct random
+    slots, page-aligned runs, pads and invalid slots, with rows drawn per token
+    from normal, heavy-tailed, zero, subnormal and one-outlier distributions."""
+    import torch
+    rng = np.random.default_rng(9000 + seed)
+    R = int(rng.integers(1, 9))
+    L = int(rng.integers(1, 4))
+    pages = int(rng.integers(4, 80))
+    guard = int(rng.choice([0, 16, 64, 128]))
+    layout = CacheLayout(replicas=R, layers=L, num_pages=pages, guard=guard)
+    T = int(rng.integers(1, min(layout.capacity, 4000) + 1))
+    LS, RS, IS = (512 + 8 * int(rng.integers(0, 4)), 64 + 8 * int(rng.integers(0, 4)),
+                  128 + 8 * int(rng.integers(0, 4)))
+    layer = int(rng.integers(0, L))
+    # slots: runs of consecutive slots from page starts, then random distinct slots
+    slots = np.empty(0, np.int64)
+    free_pages = list(rng.permutation(pages))
+    while slots.size < T // 2 and free_pages:
+        p = free_pages.pop()
+        n = int(rng.integers(1, 65))
+        slots = np.concatenate([slots, p * 64 + np.arange(n)])
+    used = set(slots.tolist())
+    rest = np.array([s for s in rng.permutation(layout.capacity) if s not in used][:T - slots.size], np.int64)
+    slots = np.concatenate([slots, rest])[:T]
+    if T > 3:
+        slots[rng.choice(T, T // 7, replace=False)] = -1
+        bad = rng.choice(T, max(1, T // 50), replace=False)
+        slots[bad] = np.where(rng.random(bad.size) < 0.5, layout.capacity + rng.integers(0, 99, bad.size),
+                              -2 - rng.integers(0, 99, bad.size))
+    wide_l, wide_r, wide_i = _random_rows(rng, T, LS), rng.integers(0, 65536, (T, RS), dtype=np.uint16), \
+        _random_rows(rng, T, IS)
+    x = LayerInputs(np.ascontiguousarray(wide_l[:, :512]), np.ascontiguousarray(wide_r[:, :64]),
+                    np.ascontiguousarray(wide_i[:, :128]), slots)
+    G.log(f"random config {seed}: R={R} L={L} pages={pages} guard={guard} T={T} strides {LS}/{RS}/{IS} layer={layer}")
+    dev = G.DeviceCache(layout)
+    try:
+        dl, dr, di = G.to_dev_u16(wide_l), G.to_dev_u16(wide_r), G.to_dev_u16(wide_i)
+        ds = G.to_dev_i64(slots)
+        kvpub.check(kvpub.kvpub_store(dev.ctx, layer, T, dl.data_ptr(), LS, dr.data_ptr(), RS, di.data_ptr(),
+                                      IS, ds.data_ptr(), torch.cuda.current_stream().cuda_stream), "kvpub_store")
+        st, invalid, flags = dev.errors()
+        kvpub.check(st, "kvpub_error_read")
+        mains, idxs, want_invalid = G.oracle_replicas(orc, layout, [(layer, x)])
+        assert invalid == want_invalid and flags == 0
+        G.assert_full_parity(dev, mains, idxs)
+    finally:
+        dev.free()
