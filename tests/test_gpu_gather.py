@@ -169,3 +169,73 @@ def test_gather_bad_arguments():
     torch().cuda.synchronize()
     assert np.all(out.host()[0] == CANARY), "a rejected call wrote output"
     dev.free()
+
+
+def _random_cache_bytes(rng, layout):
+    """One replica's Main-KV and Indexer-K buffers holding arbitrary bytes of the
+    documented format: any e4m3 code but the NaN ones, tile scales drawn from zero,
+    binary32 subnormals and normal values from 2^-126 to 2^100, any RoPE bits."""
+    L = layout
+    m = rng.integers(0, 256, size=L.main_bytes, dtype=np.uint8)
+    i = rng.integers(0, 256, size=L.idx_bytes, dtype=np.uint8)
+
+    def scales(n):
+        e = rng.uniform(-149, 100, size=n)
+        v = (2.0 ** e * rng.uniform(1, 2, size=n)).astype(np.float32)
+        v[rng.random(n) < 0.05] = 0.0
+        return v.view(np.uint8).reshape(n, 4)
+
+    for l in range(L.layers):
+        for p in range(L.num_pages):
+            base = l * L.main_layer_stride + p * L.main_page_stride
+            rows = m[base:base + 64 * 656].reshape(64, 656)
+            codes = rows[:, :512]
+            codes[(codes & 0x7F) == 0x7F] &= 0xFE
+            rows[:, 512:528] = scales(64 * 4).reshape(64, 16)
+            ib = l * L.idx_layer_stride + p * L.idx_page_stride
+            icodes = i[ib:ib + 8192]
+            icodes[(icodes & 0x7F) == 0x7F] &= 0xFE
+            i[ib + 8192:ib + 8448] = scales(64).reshape(-1)
+    return m, i
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gather_random_caches(orc, seed):
+    """Seeded random layouts (replicas, layers, pages, guard bytes) filled with
+    arbitrary bytes of the documented format, gathered from a random replica and
+    layer with repeated, unordered, padded and out-of-range slots into strided
+    outputs, bit for bit against the oracle's gather of the same bytes."""
+    t = torch()
+    rng = np.random.default_rng(7000 + seed)
+    layout = W.CacheLayout(replicas=int(rng.integers(1, 5)), layers=int(rng.integers(1, 4)),
+                           num_pages=int(rng.integers(2, 40)), guard=int(rng.choice([0, 16, 64])))
+    T = int(rng.integers(1, 3000))
+    replica, layer = int(rng.integers(0, layout.replicas)), int(rng.integers(0, layout.layers))
+    log(f"gather random cache {seed}: R={layout.replicas} L={layout.layers} pages={layout.num_pages} "
+        f"guard={layout.guard} T={T} replica={replica} layer={layer}")
+    dev = DeviceCache(layout)
+    try:
+        host = [_random_cache_bytes(rng, layout) for _ in range(layout.replicas)]
+        for r, (m, i) in enumerate(host):
+            dev.main[r].copy_(t.from_numpy(m))
+            dev.idx[r].copy_(t.from_numpy(i))
+        slots = rng.integers(0, layout.capacity, size=T).astype(np.int64)
+        if T > 4:
+            slots[rng.choice(T, T // 6, replace=False)] = -1
+            bad = rng.choice(T, max(1, T // 40), replace=False)
+            slots[bad] = np.where(rng.random(bad.size) < 0.5, layout.capacity + rng.integers(0, 99, bad.size),
+                                  -2 - rng.integers(0, 99, bad.size))
+        out = Outputs(T, ls=512 + 8 * int(rng.integers(0, 3)), rs=64 + 8 * int(rng.integers(0, 3)),
+                      is_=128 + 8 * int(rng.integers(0, 3)))
+        kvpub.check(gather(dev, out, replica, layer, to_dev_i64(slots), T), "kvpub_gather")
+        L = layout
+        want = orc.gather(host[replica][0], host[replica][1], num_pages=L.num_pages,
+                          main_page_stride=L.main_page_stride, main_layer_stride=L.main_layer_stride,
+                          idx_page_stride=L.idx_page_stride, idx_layer_stride=L.idx_layer_stride, layer=layer,
+                          slot_mapping=slots)
+        check(out, want, f"random cache {seed}")
+        st, invalid, _ = dev.errors(clear=True)
+        kvpub.check(st)
+        assert invalid == want[3]
+    finally:
+        dev.free()
