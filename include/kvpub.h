@@ -242,10 +242,13 @@ KVPUB_API kvpub_status kvpub_vmm_destroy(kvpub_vmm *vmm);
 
 /* One fence on `lane`, asynchronously on `stream`: a single one-wavefront
  * kernel that adds 1 to the lane's device epoch with a system-scope
- * acquire-release read-modify-write.  With one participant that is the whole
- * fence.  With peers it then publishes the new value as this participant's
- * signal and acquire-waits until every other participant's signal has
- * reached it.  The expected value is never a kernel argument, so a captured
+ * read-modify-write that releases every write made on this GPU before the
+ * fence.  With one participant that release RMW is the whole fence (no other
+ * agent publishes into this GPU's memory; work after the fence runs in later
+ * kernels, ordered by their own acquire at dispatch).  With peers the RMW
+ * also acquires, then the kernel publishes the new value as this
+ * participant's signal and acquire-waits until every other participant's
+ * signal has reached it.  The expected value is never a kernel argument, so a captured
  * fence advances the epoch on every replay.  If the wait exceeds
  * fence_timeout_ns the kernel records KVPUB_FLAG_FENCE_TIMEOUT |
  * KVPUB_FLAG_POISONED and returns; from then on stores and fences of this

@@ -10,12 +10,13 @@
 // overlapped micro-batches.
 //
 // Protocol per lane, run by lane 0 of one wavefront:
-//   e = epoch[lane] + 1, by an acquire-release RMW at system scope: every
-//       write this GPU made before the fence is visible before the epoch
-//       moves, and what was published before it is visible after;
+//   e = epoch[lane] + 1, by an RMW at system scope with release semantics:
+//       every write this GPU made before the fence is visible before the
+//       epoch moves (with peers also acquire: what was published before it is
+//       visible after);
 //   with peers only: signal[self] = e (a release store), then for every
 //       other participant q: acquire-load signal[q] until it is >= e.
-// Alone (one participant) the RMW is the whole fence.
+// Alone (one participant) the release RMW is the whole fence.
 // This GPU's own signal is never awaited: it was written just before, in
 // program order, by the same wave.  The expected value e is read from device
 // memory, never passed as a kernel argument, so replaying a captured launch
@@ -35,12 +36,16 @@ __global__ __launch_bounds__(64) void fence_kernel(uint64_t* epoch, uint64_t* si
                                                    uint64_t timeout_ticks) {
     if (threadIdx.x != 0) return;
     if (num_participants == 1) {
-        // Alone, the epoch is the whole barrier: the acquire-release RMW
-        // publishes this GPU's writes and acquires what was published before.
-        // Only a fence waiting for peers can time out and poison the context,
-        // so there is no status to check first (one memory round trip, not two)
-        // and no signal for anyone to read.
-        __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM);
+        // Alone, the epoch is the whole barrier: a release RMW at system scope
+        // publishes every write this GPU made before the fence, then the epoch
+        // moves.  The acquire half has nothing to act on: no other agent
+        // publishes into this GPU's memory, and this wave ends right after the
+        // RMW, so work after the fence runs in later kernels, which are ordered
+        // by their own acquire at dispatch (an acquire here would only
+        // invalidate the L2 for them).  Only a fence waiting for peers can time
+        // out and poison the context, so there is no status to check first (one
+        // memory round trip) and no signal for anyone to read.
+        __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         return;
     }
     if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kStatusPoisoned) return;
