@@ -90,7 +90,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the replicas of this path are buffers in one GPU's "
-              "HBM and no multi-GPU run is part of this build; use --gpus 1", file=sys.stderr)
+              "HBM, and publication across GPUs is not implemented; use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
