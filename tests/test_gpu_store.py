@@ -545,3 +545,38 @@ def test_random_configurations(orc, seed):
         G.assert_full_parity(dev, mains, idxs)
     finally:
         dev.free()
+
+
+@pytest.mark.parametrize("T", [500, 3000, 11000])
+def test_fused_fanout_equals_per_replica_stores(orc, T):
+    """The pages' A/B, checked for equal output: one store launch writing all four
+    replicas, and four single-replica contexts over other buffers each storing the
+    same rows (an insert per replica), leave byte-identical replicas equal to the
+    oracle's.  At T=11000 the fused launch writes 34.7 MB (write-through path)
+    while each single-replica launch writes 8.7 MB (streamed path)."""
+    import torch
+    rng = np.random.default_rng(606 + T)
+    R = 4
+    layout = CacheLayout(replicas=R, layers=1, num_pages=(T + 63) // 64 + 8)
+    slots = rng.permutation(layout.capacity)[:T].astype(np.int64)
+    slots[::53] = -1
+    x = LayerInputs(*W._normal_rows(rng, T), slots)
+    G.log(f"fan-out A/B parity: T={T}, R={R} fused vs {R} single-replica stores")
+    fused = G.DeviceCache(layout)
+    single_layout = CacheLayout(replicas=1, layers=1, num_pages=layout.num_pages)
+    singles = [G.DeviceCache(single_layout) for _ in range(R)]
+    try:
+        d = G.DeviceInputs(x)
+        kvpub.check(fused.store(0, d), "fused store")
+        for sc in singles:
+            kvpub.check(sc.store(0, d), "single-replica store")
+        torch.cuda.synchronize()
+        mains, idxs, _ = G.oracle_replicas(orc, layout, [(0, x)])
+        G.assert_full_parity(fused, mains, idxs)
+        for r, sc in enumerate(singles):
+            gm, gi = sc.host()
+            assert np.array_equal(gm[0], mains[r]) and np.array_equal(gi[0], idxs[r]), f"single-replica store {r}"
+    finally:
+        fused.free()
+        for sc in singles:
+            sc.free()
