@@ -199,7 +199,7 @@ def _random_cache_bytes(rng, layout):
     return m, i
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(24))
 def test_gather_random_caches(orc, seed):
     """Seeded random layouts (replicas, layers, pages, guard bytes) filled with
     arbitrary bytes of the documented format, gathered from a random replica and

@@ -493,7 +493,7 @@ def _random_rows(rng, T, width):
     return bf16_bits(x.astype(np.float32))
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_configurations(orc, seed):
     """Seeded random configurations, whole buffers against the oracle: replica
     count, layer count, pages, guard bytes after each page (page strides above
