@@ -447,3 +447,38 @@ def test_vmm_one_layer_write_through_graph_follows_growth(orc):
         if graph is not None:
             kvpub.kvpub_graph_destroy(graph)
         kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
+
+
+def test_vmm_heavy_full_size(orc):
+    """The heavy-tail store shape on VMM-backed replicas, as the benchmark times it
+    (T=32,768 tokens, R=4, 16,384 pages, one launch on the write-through path):
+    every backed byte of every replica against the oracle."""
+    layout, x = W.heavy()
+    R, P = layout.replicas, layout.num_pages
+    G.log(f"vmm heavy full size: T={x.slots.size} R={R} pages={P}")
+    t = G.torch()
+    hip = G.hip_runtime()
+    cfg = kvpub.kvpub_config_init(R, 1, P)
+    st, vmm, mb, ib = kvpub.kvpub_vmm_create(cfg, P)
+    kvpub.check(st, "kvpub_vmm_create")
+    try:
+        fill_pages(hip, cfg, mb, ib, 0, P, 1)
+        st, ctx = kvpub.kvpub_create(cfg, mb, ib)
+        kvpub.check(st)
+        d = G.DeviceInputs(x)
+        assert d.T * R * 788 > 32 << 20                            # the write-through path
+        kvpub.check(kvpub.kvpub_store(ctx, 0, d.T, d.latent.data_ptr(), 512, d.rope.data_ptr(), 64,
+                                      d.indexer.data_ptr(), 128, d.slots.data_ptr(),
+                                      t.cuda.current_stream().cuda_stream), "kvpub_store")
+        t.cuda.synchronize()
+        st, invalid, flags = kvpub.kvpub_error_read(ctx, False)
+        kvpub.check(st)
+        assert invalid == 0 and flags == 0
+        G.log("vmm heavy full size: oracle")
+        mirror = Mirror(cfg, 1)
+        assert mirror.store(orc, P, 0, x) == 0
+        G.log("vmm heavy full size: compare every backed byte")
+        compare_backed(hip, cfg, mb, ib, mirror, P, 1, "heavy on VMM-backed replicas")
+        kvpub.check(kvpub.kvpub_destroy(ctx))
+    finally:
+        kvpub.check(kvpub.kvpub_vmm_destroy(vmm))
