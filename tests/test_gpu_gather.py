@@ -239,3 +239,26 @@ def test_gather_random_caches(orc, seed):
         assert invalid == want[3]
     finally:
         dev.free()
+
+
+def test_gather_graph_layer_full_size(orc):
+    """The reader side at the size the benchmark times: one layer of the graph
+    workload (R=2, 8,192 pages; T=4,096 tokens at page-permuted slots) stored with
+    kvpub_store, then all 4,096 rows gathered from each replica, bit for bit
+    against the oracle's gather of the same replica bytes."""
+    rng = np.random.default_rng(808)
+    layout = W.CacheLayout(replicas=2, layers=1, num_pages=W.graph_layout().num_pages)
+    slots = W.graph_slots()
+    T = slots.size
+    x = W.LayerInputs(*W._normal_rows(rng, T), slots)
+    log(f"gather, graph layer full size: T={T}, R=2, pages={layout.num_pages}")
+    dev = DeviceCache(layout)
+    try:
+        kvpub.check(dev.store(0, DeviceInputs(x)), "kvpub_store")
+        sd = to_dev_i64(slots)
+        for replica in range(layout.replicas):
+            out = Outputs(T)
+            kvpub.check(gather(dev, out, replica, 0, sd, T), "kvpub_gather")
+            check(out, oracle_gather(orc, dev, replica, 0, slots), f"graph layer, replica {replica}")
+    finally:
+        dev.free()
