@@ -209,9 +209,21 @@ void kvo_quant_tile(const uint16_t *x, uint8_t *codes, float *scale_out)
         *scale_out = 0.0f;
         return;
     }
+#if defined(KVO_PLANT) && KVO_PLANT == 17
+    scale = amax * (1.0f / KVO_E4M3_MAX_VALUE);    /* planted: multiply by RN(1/448) */
+#else
     scale = amax / KVO_E4M3_MAX_VALUE;
+#endif
+#if defined(KVO_PLANT) && KVO_PLANT == 18
+    {
+        const float inv = 1.0f / scale;            /* planted: quotient by reciprocal multiply */
+        for (k = 0; k < KVO_TILE; ++k)
+            codes[k] = kvo_e4m3_encode(bf16_to_float(x[k]) * inv);
+    }
+#else
     for (k = 0; k < KVO_TILE; ++k)
         codes[k] = kvo_e4m3_encode(bf16_to_float(x[k]) / scale);
+#endif
     *scale_out = scale;
 }
 

@@ -25,13 +25,14 @@
 // code = e4m3fn(RN32(x / scale)).  The scale and its reciprocal y =
 // RN32(1/scale) come from a short exact sequence (tile_scale), run once for a
 // group's 20 tiles: each lane of a DPP row takes one of the row's five tiles,
-// and row_newbcast hands each round's values back to the row.  RN32(x/scale)
-// is computed as
+// and row_newbcast hands each round's values back to the row.  In place of
+// the division the quotient is
 // q = x*y, t = fma(q, scale, -x), q' = fma(-t, y, q), which is the magnitude
 // form fma(fma(-|x|y, scale, |x|), y, |x|y) with the sign of x put back.
-// For every scale >= 2^-64 this gives the same e4m3 code as a correctly
-// rounded division for every bf16 x with |x| <= amax (the domain is finite
-// and was checked exhaustively on the CPU); tiles with a smaller scale (and
+// q' is not always RN32(x/scale) (it can differ in the last bit), but for
+// every scale >= 2^-64 and every bf16 x with |x| <= amax it has the same e4m3
+// code as the correctly rounded division: the domain is finite (9.8e8 signed
+// pairs) and a CPU test walks all of it; tiles with a smaller scale (and
 // all-zero tiles) take the plain IEEE division path.  The conversion uses the
 // gfx950 OCP e4m3 convert (round-to-nearest-even, saturating only above 464):
 // |x/scale| <= 448 (1 + 2^-23) for finite input, so no clamp is needed.
@@ -217,10 +218,11 @@ __device__ __forceinline__ TileScale tile_scale(uint32_t ab) {
 }
 constexpr uint32_t kFastMinExponent = 72;   // amax >= 2^-55  <=>  scale >= 2^-64
 
-// RN32(x / scale) from the correctly rounded reciprocal y (see the header):
-// q = x*y, t = q*scale - x (exact, fused), q' = q - t*y.  Round-to-nearest
-// is symmetric, so this is the magnitude computation with the sign of x put
-// back, signed zeros included (x = -0 gives t = +0 and q' = -0).
+// A quotient with the e4m3 code of RN32(x / scale), from the correctly rounded
+// reciprocal y (see the header): q = x*y, t = q*scale - x (exact, fused),
+// q' = q - t*y.  Round-to-nearest is symmetric, so this is the magnitude
+// computation with the sign of x put back, signed zeros included (x = -0
+// gives t = +0 and q' = -0).
 __device__ __forceinline__ float quotient_fast(float x, float scale, float y) {
     const float q = x * y;
     const float t = __builtin_fmaf(q, scale, -x);

@@ -13,6 +13,10 @@ from the oracle itself:
 * tile invariants: the element of largest magnitude maps to +-448 (0x7E),
   dequantized values lie within half an e4m3 step (at the tile scale) of
   the input, the chosen code is the nearest one, exact tiles round-trip;
+* exact binary32 arithmetic of the tile: the scale bits equal RN32(amax/448)
+  from exact rational rounding (all 128 bf16 mantissas, binary32-subnormal
+  scales included), and each code is the encoding of the exactly rounded
+  quotient RN32(x/scale) over every bf16 magnitude up to several amax values;
 * layout invariants of the store: replicas identical, RoPE bits verbatim,
   each row dequantizes to its token's input at the documented offsets,
   every byte outside the written rows unchanged, invalid slots counted,
@@ -257,6 +261,94 @@ def pin_tile_nearest(orc):
         ok = (nb >= 0) & (nb <= 0x7E) & nz[:, None]
         en = np.abs(q - sgn * e4m3_decode(np.where(ok, nb, 0)))
         assert not np.any(ok & (err > en + slack)), "code not nearest to x/scale"
+
+
+# Exponent fields of the amax values the exact pins sweep (bf16 biased exponents):
+# 0 is a bf16 subnormal amax; up to 9 the scale amax/448 is a binary32 subnormal;
+# 71/72 straddle the smallest scale (2^-64) of the kernels' division-free path;
+# 254 is the largest finite binade.
+EXACT_AMAX_EXPONENTS = (0, 1, 2, 8, 9, 10, 11, 40, 71, 72, 73, 100, 126, 127, 128, 134, 135, 200, 253, 254)
+
+
+def _tiles_with_amax(rng, amax_bits, n_per):
+    """n_per tiles for each positive bf16 amax pattern: element 0 is +-amax, the
+    other 127 are random bf16 values of magnitude <= amax (uniform over the bit
+    patterns, which order like the magnitudes), random signs."""
+    ab = np.repeat(np.asarray(amax_bits, dtype=np.int64), n_per)
+    mags = (rng.random((ab.size, 128)) * (ab[:, None] + 1)).astype(np.int64)
+    mags[:, 0] = ab
+    signs = rng.integers(0, 2, size=mags.shape).astype(np.int64) << 15
+    return (mags | signs).astype(np.uint16)
+
+
+def pin_tile_scale_exact(orc):
+    """The stored tile scale is RN32(amax / 448) bit for bit (reading: binary32
+    division, round to nearest even, subnormals kept), against an exact rational
+    rounding, for all 128 bf16 mantissas at exponents from a bf16 subnormal amax
+    (binary32-subnormal scales) to the largest binade; and every code is the e4m3
+    encoding of RN32(x / scale), the quotient rounded exactly."""
+    from fractions import Fraction
+    from exact_fp import rn32, rn32_div, f32_bits
+    rng = np.random.default_rng(21)
+    amax_bits = [(e << 7) | m for e in EXACT_AMAX_EXPONENTS for m in range(128) if (e << 7) | m]
+    bits = _tiles_with_amax(rng, amax_bits, 1)
+    codes, scales = orc.quant_tiles(bits)
+    want = np.array([rn32(Fraction(float(bf16_to_f32(np.uint16(a)))) / 448) for a in amax_bits], np.float32)
+    bad = np.nonzero(scales.view(np.uint32) != want.view(np.uint32))[0]
+    assert bad.size == 0, f"{bad.size} scales differ from RN32(amax/448), e.g. " + ", ".join(
+        f"amax {amax_bits[i]:#06x}: {float(scales[i]).hex()} want {float(want[i]).hex()}" for i in bad[:4])
+    assert np.any((want > 0) & (want < np.finfo(np.float32).tiny)), "no binary32-subnormal scale swept"
+    # the quotient, rounded exactly, then the independent bit-level encoder
+    x = bf16_to_f32(bits)
+    q = rn32_div(x, want[:, None])
+    want_codes = e4m3_encode_bits(q)
+    bad = np.argwhere(codes != want_codes)
+    assert bad.size == 0, f"{len(bad)} codes differ from e4m3(RN32(x/scale)), e.g. " + ", ".join(
+        f"x {float(x[i, j]).hex()} / {float(want[i]).hex()}: {codes[i, j]:#04x} want {want_codes[i, j]:#04x}"
+        for i, j in bad[:4])
+    # the integer divider itself agrees with exact rational rounding on a sample
+    # (magnitudes: a Fraction has no signed zero)
+    for i, j in zip(rng.integers(0, len(amax_bits), 300), rng.integers(0, 128, 300)):
+        exact = rn32(abs(Fraction(float(x[i, j]))) / Fraction(float(want[i])))
+        assert f32_bits(abs(float(q[i, j]))) == f32_bits(exact), (float(x[i, j]), float(want[i]))
+
+
+# amax values whose tiles cover every bf16 magnitude up to them (both signs):
+# scale 1 (448), a scale with a long binary expansion (1.0 -> RN32(1/448)), the
+# next pattern above 448, a mid exponent, the smallest fast-path amax, a
+# binary32-subnormal scale, the smallest bf16 subnormal and the largest bf16;
+# and three mantissas (0x0A, 0x44, 0x18) for which a multiply by RN32(1/scale)
+# lands on the other side of an e4m3 rounding boundary than RN32(x/scale) does
+# for some x (15, 30 and 15 values; found by exhaustive search over all 128).
+SWEEP_AMAX_BITS = (0x43E0, 0x3F80, 0x43E1, 0x4049, 0x2400, 0x0480, 0x0001, 0x7F7F, 0x3B9D, 0x5F11,
+                   0x3F8A, 0x3FC4, 0x4A98)
+
+
+def pin_tile_quotient_sweep(orc):
+    """Over every bf16 magnitude up to each of several amax values (both signs),
+    the tile's codes are e4m3(RN32(x / RN32(amax / 448))) with both roundings
+    exact: catches a reciprocal multiply, a contracted or reordered quotient."""
+    from fractions import Fraction
+    from exact_fp import rn32, rn32_div
+    rng = np.random.default_rng(22)
+    failures = []
+    for ab in SWEEP_AMAX_BITS:
+        mags = np.arange(ab + 1, dtype=np.int64)
+        vals = np.concatenate([mags, mags | 0x8000])
+        vals = vals[rng.permutation(vals.size)]
+        n_tiles = -(-vals.size // 127)
+        body = np.resize(vals, n_tiles * 127).reshape(n_tiles, 127)     # wraps: every value at least once
+        bits = np.concatenate([np.full((n_tiles, 1), ab), body], axis=1).astype(np.uint16)
+        codes, scales = orc.quant_tiles(bits)
+        scale = np.float32(rn32(Fraction(float(bf16_to_f32(np.uint16(ab)))) / 448))
+        assert np.all(scales.view(np.uint32) == np.uint32(scale.view(np.uint32))), f"amax {ab:#06x}: scale"
+        x = bf16_to_f32(bits)
+        want = e4m3_encode_bits(rn32_div(x, scale))
+        bad = np.argwhere(codes != want)
+        if bad.size:
+            failures.append(f"amax {ab:#06x}: {len(bad)} codes differ from e4m3(RN32(x/scale)), e.g. " + ", ".join(
+                f"{float(x[i, j]).hex()}: {codes[i, j]:#04x} want {want[i, j]:#04x}" for i, j in bad[:2]))
+    assert not failures, "; ".join(failures)
 
 
 def pin_tile_special(orc):
@@ -538,5 +630,6 @@ def pin_epoch(orc):
 
 ALL_PINS = [pin_hand_codes, pin_encoder_bruteforce, pin_encoder_torch, pin_encoder_nearest,
             pin_tile_exact, pin_tile_invariants, pin_tile_nearest, pin_tile_special,
+            pin_tile_scale_exact, pin_tile_quotient_sweep,
             pin_layout, pin_layout_order_and_fanout, pin_store_empty, pin_epoch,
             pin_gather_hand_values, pin_gather_roundtrip_exact, pin_gather_bound_and_pads]

@@ -16,44 +16,16 @@ the kernel's fast path, so that a change to either is caught without a GPU:
   rounded quotient RN(x / s) (the OCP e4m3 encoding, round to nearest even).
 """
 from fractions import Fraction
-import struct
 
 import numpy as np
 import pytest
+
+from exact_fp import f32_bits as bits, f32_from_bits as from_bits, rn32
 
 
 def f32(v) -> float:
     """Round a Python float (binary64) to binary32, returned as a float."""
     return float(np.float32(v))
-
-
-def bits(v: float) -> int:
-    return struct.unpack("<I", struct.pack("<f", v))[0]
-
-
-def from_bits(u: int) -> float:
-    return struct.unpack("<f", struct.pack("<I", u & 0xFFFFFFFF))[0]
-
-
-def rn32(x: Fraction) -> float:
-    """Exact rational -> binary32, round to nearest, ties to even (finite range)."""
-    if x == 0:
-        return 0.0
-    neg = x < 0
-    m = -x if neg else x
-    e = m.numerator.bit_length() - m.denominator.bit_length()
-    if Fraction(2) ** e > m:
-        e -= 1
-    while Fraction(2) ** (e + 1) <= m:
-        e += 1
-    q_exp = max(e, -126) - 23                     # quantum of the binade (subnormals: 2^-149)
-    quantum = Fraction(2) ** q_exp
-    n, rem = divmod(m, quantum)                   # n integer part, rem in [0, quantum)
-    n = int(n)
-    if rem * 2 > quantum or (rem * 2 == quantum and n % 2 == 1):
-        n += 1
-    v = float(n * quantum)                        # exact in binary64
-    return -v if neg else v
 
 
 def fma32(a: float, b: float, c: float) -> float:

@@ -4,7 +4,8 @@ Each ``KVO_PLANT`` variant of ``oracle/kvpub_oracle.c`` is a plausible slip:
 ties away from zero, overflow to NaN, a dropped sign, a wrong range constant,
 an amax that skips an element, scales or RoPE bytes out of order, a wrong
 scale offset, page and offset swapped, pads counted as invalid, a replica
-skipped, a wrong subnormal step, truncation instead of rounding; on the
+skipped, a wrong subnormal step, truncation instead of rounding, the tile
+scale as a multiply by RN(1/448), the quotient as a multiply by RN(1/scale); on the
 reader side a sign dropped on decode, bf16 truncation, scales of the wrong
 tile."""
 import pytest
@@ -12,7 +13,7 @@ import pytest
 import oracle
 import pins
 
-PLANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16]
+PLANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18]
 
 
 @pytest.mark.parametrize("plant", PLANTS)
