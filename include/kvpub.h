@@ -127,13 +127,24 @@ typedef struct {
     uint32_t num_participants;  /* fence participants, 1..8; > 1 only with host-driven peers (tests) */
     uint64_t fence_timeout_ns;  /* 0 = 5 s */
     int32_t device;             /* HIP device ordinal */
-    uint32_t flags;             /* reserved, must be 0 */
+    uint32_t flags;             /* 0 or KVPUB_CONFIG_FENCE_ACQUIRE_WAIT; other bits must be 0 */
 } kvpub_config;
+
 /* With L == 1 the layer strides address nothing and are not checked; a value
  * above num_pages * page stride states the span the layer may grow into
  * (kvpub_vmm_create sets it to the reserved range), which large stores use as
  * the bound of their write-through buffer range.  Any value is safe: no store
  * goes beyond the context's capacity. */
+
+/* kvpub_config.flags: with one participant, kvpub_fence follows its release
+ * RMW with acquire loads of the lane's epoch until it holds the value the RMW
+ * produced -- the system-scope release/acquire pair of vLLM PR #52863, Design
+ * (device-epoch barrier), taken literally.  Without the flag a one-participant
+ * fence is the release RMW alone (no other agent publishes into this GPU's
+ * memory, and work after the fence runs in later kernels, which the queue
+ * orders with its own acquire at dispatch).  No effect with peers: their fence
+ * always acquire-waits. */
+#define KVPUB_CONFIG_FENCE_ACQUIRE_WAIT 0x1u
 
 /* Fill *cfg with defaults for R replicas of L layers of num_pages dense pages:
  * page strides 41984 / 8448, layer strides num_pages * page stride, one lane,
@@ -255,6 +266,24 @@ KVPUB_API kvpub_status kvpub_vmm_destroy(kvpub_vmm *vmm);
  * context write nothing (fail-closed; only a fence with peers can time out).
  * No allocation and no synchronization: safe under stream capture. */
 KVPUB_API kvpub_status kvpub_fence(kvpub_ctx *ctx, uint32_t lane, kvpub_stream_t stream);
+
+/* The pages' earlier fence, kept for comparison: two launches per fence and an
+ * epoch held on the host (vLLM PR #54030 "[Perf][PCP] Fuse direct-KV
+ * publication fence", Motivation and commit list: the fence used to be a
+ * signal launch and a wait launch, and because the epoch lived on the host a
+ * captured graph could not advance it on replay).  The context keeps a host
+ * counter per lane; each call takes e = counter + 1 and enqueues on `stream` a
+ * kernel that release-stores e into the lane's device epoch at system scope,
+ * then a kernel that acquire-loads it until it is >= e (bounded by
+ * fence_timeout_ns; a timeout sets KVPUB_FLAG_FENCE_TIMEOUT |
+ * KVPUB_FLAG_POISONED), and the counter becomes e.  Under stream capture the
+ * counter moves once, at capture: every replay publishes the captured values
+ * again, so the device epoch stops advancing -- the failure the single-launch
+ * kvpub_fence removes.  kvpub_epoch_read shows the published value.  Do not
+ * mix it with kvpub_fence on one lane (the two count independently).  One
+ * participant only (KVPUB_ERR_UNSUPPORTED otherwise).  No allocation and no
+ * synchronization; the counter is not thread-safe. */
+KVPUB_API kvpub_status kvpub_fence_host_epoch(kvpub_ctx *ctx, uint32_t lane, kvpub_stream_t stream);
 
 /* One layer of a captured sequence. */
 typedef struct {

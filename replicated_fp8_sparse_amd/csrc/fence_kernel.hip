@@ -16,7 +16,10 @@
 //       visible after);
 //   with peers only: signal[self] = e (a release store), then for every
 //       other participant q: acquire-load signal[q] until it is >= e.
-// Alone (one participant) the release RMW is the whole fence.
+// Alone (one participant) the release RMW is the whole fence by default; a
+// context created with the acquire-wait option follows it with acquire loads
+// of the epoch itself until it is >= e (with one participant the epoch is the
+// only signal), the release/acquire pair the Design section describes.
 // This GPU's own signal is never awaited: it was written just before, in
 // program order, by the same wave.  The expected value e is read from device
 // memory, never passed as a kernel argument, so replaying a captured launch
@@ -30,11 +33,36 @@
 namespace kvpub {
 namespace {
 
+// Bounded acquire wait until *w >= e; on timeout the context's sticky timeout
+// and poisoned flags are set.  Returns false on timeout.
+__device__ __forceinline__ bool wait_at_least(const uint64_t* w, uint64_t e, uint32_t* status,
+                                              uint64_t start, uint64_t timeout_ticks) {
+    while (__hip_atomic_load(w, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < e) {
+        if (wall_clock64() - start > timeout_ticks) {
+            __hip_atomic_fetch_or(status, kStatusFenceTimeout | kStatusPoisoned, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_SYSTEM);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+}
+
 // Plain scalar arguments, so that they arrive preloaded in SGPRs.
 __global__ __launch_bounds__(64) void fence_kernel(uint64_t* epoch, uint64_t* signals, uint32_t* status,
                                                    uint32_t num_participants, uint32_t self,
-                                                   uint64_t timeout_ticks) {
+                                                   uint64_t timeout_ticks, uint32_t acquire_wait) {
     if (threadIdx.x != 0) return;
+    if (num_participants == 1 && acquire_wait) {
+        // Release RMW, then acquire loads of the epoch until it has reached the
+        // value this fence moved it to.  The RMW's result already shows that
+        // value, so the first load passes unless the epoch was moved back (by a
+        // host-epoch fence on the same lane); the wait is bounded all the same.
+        const uint64_t e =
+            __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM) + 1;
+        (void)wait_at_least(epoch, e, status, wall_clock64(), timeout_ticks);
+        return;
+    }
     if (num_participants == 1) {
         // Alone, the epoch is the whole barrier: a release RMW at system scope
         // publishes every write this GPU made before the fence, then the epoch
@@ -56,16 +84,28 @@ __global__ __launch_bounds__(64) void fence_kernel(uint64_t* epoch, uint64_t* si
     const uint64_t start = wall_clock64();
     for (uint32_t q = 0; q < num_participants; ++q) {
         if (q == self) continue;
-        const uint64_t* sig = signals + (size_t)q * kSignalStride;
-        while (__hip_atomic_load(sig, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) < e) {
-            if (wall_clock64() - start > timeout_ticks) {
-                __hip_atomic_fetch_or(status, kStatusFenceTimeout | kStatusPoisoned, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_SYSTEM);
-                return;
-            }
-            __builtin_amdgcn_s_sleep(2);
-        }
+        if (!wait_at_least(signals + (size_t)q * kSignalStride, e, status, start, timeout_ticks)) return;
     }
+}
+
+// The two-launch fence with a host-held epoch (PR #54030 Motivation: the
+// design that the single-launch fence replaces, kept to reproduce the pages'
+// comparison).  The host counts the epoch and passes the value e to both
+// kernels as an argument: the first publishes it with a system-scope release
+// store, the second acquire-waits until the word holds at least e.  A captured
+// pair therefore carries the value of its capture: replays publish the same e
+// again and the epoch does not advance.  With one participant only; like the
+// one-participant single-launch fence, the publication does not read the
+// status word.
+__global__ __launch_bounds__(64) void host_epoch_publish_kernel(uint64_t* epoch, uint64_t e) {
+    if (threadIdx.x != 0) return;
+    __hip_atomic_store(epoch, e, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__global__ __launch_bounds__(64) void host_epoch_wait_kernel(const uint64_t* epoch, uint32_t* status, uint64_t e,
+                                                             uint64_t timeout_ticks) {
+    if (threadIdx.x != 0) return;
+    (void)wait_at_least(epoch, e, status, wall_clock64(), timeout_ticks);
 }
 
 }  // namespace
@@ -73,7 +113,16 @@ __global__ __launch_bounds__(64) void fence_kernel(uint64_t* epoch, uint64_t* si
 hipError_t launch_fence(const FenceParams& p, hipStream_t stream) {
     (void)hipGetLastError();
     fence_kernel<<<dim3(1), dim3(64), 0, stream>>>(p.epoch, p.signals, p.status, p.num_participants, p.self,
-                                                   p.timeout_ticks);
+                                                   p.timeout_ticks, p.acquire_wait);
+    return hipGetLastError();
+}
+
+hipError_t launch_host_epoch_fence(const FenceParams& p, uint64_t e, hipStream_t stream) {
+    (void)hipGetLastError();
+    host_epoch_publish_kernel<<<dim3(1), dim3(64), 0, stream>>>(p.epoch, e);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    host_epoch_wait_kernel<<<dim3(1), dim3(64), 0, stream>>>(p.epoch, p.status, e, p.timeout_ticks);
     return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct kvpub_ctx {
     uint64_t* host_signals_dev;
     uint64_t timeout_ticks;
     hipStream_t capture_stream;
+    uint64_t host_epoch[KVPUB_MAX_LANES];   // kvpub_fence_host_epoch: the epoch each lane last published
 };
 
 struct kvpub_graph {
@@ -107,7 +108,7 @@ kvpub_status check_config(const kvpub_config* c) {
     }
     if (c->num_lanes < 1 || c->num_lanes > KVPUB_MAX_LANES) return KVPUB_ERR_INVALID_ARG;
     if (c->num_participants < 1 || c->num_participants > KVPUB_MAX_PARTICIPANTS) return KVPUB_ERR_INVALID_ARG;
-    if (c->device < 0 || c->flags != 0) return KVPUB_ERR_INVALID_ARG;
+    if (c->device < 0 || (c->flags & ~KVPUB_CONFIG_FENCE_ACQUIRE_WAIT) != 0) return KVPUB_ERR_INVALID_ARG;
     return KVPUB_OK;
 }
 
@@ -172,6 +173,7 @@ FenceParams fence_params(kvpub_ctx* ctx, uint32_t lane) {
     f.self = 0;
     f.status = reinterpret_cast<uint32_t*>(ctx->words + kvpub::kStatusOffset);
     f.timeout_ticks = ctx->timeout_ticks;
+    f.acquire_wait = (ctx->cfg.flags & KVPUB_CONFIG_FENCE_ACQUIRE_WAIT) ? 1u : 0u;
     return f;
 }
 
@@ -363,6 +365,18 @@ KVPUB_API kvpub_status kvpub_fence(kvpub_ctx* ctx, uint32_t lane, kvpub_stream_t
     DeviceGuard guard(ctx->cfg.device);
     if (!guard.ok) return KVPUB_ERR_HIP;
     return map_hip(kvpub::launch_fence(fence_params(ctx, lane), static_cast<hipStream_t>(stream)));
+}
+
+KVPUB_API kvpub_status kvpub_fence_host_epoch(kvpub_ctx* ctx, uint32_t lane, kvpub_stream_t stream) {
+    if (!ctx || lane >= ctx->cfg.num_lanes) return KVPUB_ERR_INVALID_ARG;
+    if (ctx->cfg.num_participants != 1) return KVPUB_ERR_UNSUPPORTED;
+    DeviceGuard guard(ctx->cfg.device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    const uint64_t e = ctx->host_epoch[lane] + 1;
+    const hipError_t err = kvpub::launch_host_epoch_fence(fence_params(ctx, lane), e,
+                                                          static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) ctx->host_epoch[lane] = e;
+    return map_hip(err);
 }
 
 KVPUB_API kvpub_status kvpub_graph_create(kvpub_ctx* ctx, const kvpub_layer_io* io, uint32_t n,

@@ -62,6 +62,7 @@ struct FenceParams {
     uint32_t self;               // this GPU's participant index (0)
     uint32_t* status;
     uint64_t timeout_ticks;      // in wall-clock (s_memrealtime) ticks
+    uint32_t acquire_wait;       // alone: acquire-wait on the epoch after the release RMW
 };
 
 // Enqueue one store kernel on `stream`; returns the launch status.
@@ -95,5 +96,7 @@ bool ctx_uses_storage(const kvpub_ctx* ctx, uint32_t replicas, uint8_t* const* m
 hipError_t ctx_set_pages(kvpub_ctx* ctx, uint64_t num_pages);
 // Enqueue one fence kernel on `stream`.
 hipError_t launch_fence(const FenceParams& p, hipStream_t stream);
+// Enqueue the two-launch host-epoch fence (publish e, then wait for e) on `stream`.
+hipError_t launch_host_epoch_fence(const FenceParams& p, uint64_t e, hipStream_t stream);
 
 }  // namespace kvpub

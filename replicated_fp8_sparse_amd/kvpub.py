@@ -27,6 +27,8 @@ KVPUB_ERR_FENCE_TIMEOUT = 6
 KVPUB_FLAG_FENCE_TIMEOUT = 0x1
 KVPUB_FLAG_POISONED = 0x2
 
+KVPUB_CONFIG_FENCE_ACQUIRE_WAIT = 0x1
+
 SLOTS_PER_PAGE = 64
 LATENT_DIM = 512
 ROPE_DIM = 64
@@ -39,6 +41,7 @@ MAX_REPLICAS = 8
 
 # Every function include/kvpub.h declares.
 EXPORTS = ("kvpub_config_init", "kvpub_create", "kvpub_store", "kvpub_gather", "kvpub_fence",
+           "kvpub_fence_host_epoch",
            "kvpub_graph_create", "kvpub_graph_replay", "kvpub_graph_destroy",
            "kvpub_epoch_read", "kvpub_error_read", "kvpub_participant_signal",
            "kvpub_destroy", "kvpub_strerror", "kvpub_abi_version", "kvpub_vmm_create",
@@ -102,6 +105,7 @@ def load(path=LIB_PATH):
         "kvpub_store": (i32, [vp, u32, i64, vp, i64, vp, i64, vp, i64, vp, vp]),
         "kvpub_gather": (i32, [vp, u32, u32, i64, vp, vp, i64, vp, i64, vp, i64, vp]),
         "kvpub_fence": (i32, [vp, u32, vp]),
+        "kvpub_fence_host_epoch": (i32, [vp, u32, vp]),
         "kvpub_graph_create": (i32, [vp, ctypes.POINTER(kvpub_layer_io), u32, u32, ctypes.POINTER(vp)]),
         "kvpub_graph_replay": (i32, [vp, vp]),
         "kvpub_graph_destroy": (i32, [vp]),
@@ -171,6 +175,10 @@ def kvpub_gather(ctx, replica, layer, num_tokens, slot_mapping, latent_out, late
 
 def kvpub_fence(ctx, lane=0, stream=0):
     return load().kvpub_fence(ctx, lane, stream)
+
+
+def kvpub_fence_host_epoch(ctx, lane=0, stream=0):
+    return load().kvpub_fence_host_epoch(ctx, lane, stream)
 
 
 def kvpub_graph_create(ctx, ios, lane=0):

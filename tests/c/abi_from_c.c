@@ -38,6 +38,7 @@ int main(void) {
     CHECK(kvpub_store(NULL, 0, 4, bases[0], 512, bases[0], 64, bases[0], 128, NULL, NULL) == KVPUB_ERR_INVALID_ARG);
     CHECK(kvpub_gather(NULL, 0, 0, 4, NULL, NULL, 512, NULL, 64, NULL, 128, NULL) == KVPUB_ERR_INVALID_ARG);
     CHECK(kvpub_fence(NULL, 0, NULL) == KVPUB_ERR_INVALID_ARG);
+    CHECK(kvpub_fence_host_epoch(NULL, 0, NULL) == KVPUB_ERR_INVALID_ARG);
     CHECK(kvpub_graph_replay(NULL, NULL) == KVPUB_ERR_INVALID_ARG);
     CHECK(kvpub_graph_destroy(NULL) == KVPUB_OK);
     CHECK(kvpub_destroy(NULL) == KVPUB_OK);

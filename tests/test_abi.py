@@ -62,6 +62,7 @@ def test_host_side_argument_checks():
     assert kvpub.kvpub_store(None, 0, 4, 16, 512, 16, 64, 16, 128, 16, 0) == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_gather(None, 0, 0, 4, 16, 16, 512, 16, 64, 16, 128, 0) == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_fence(None, 0, 0) == kvpub.KVPUB_ERR_INVALID_ARG
+    assert kvpub.kvpub_fence_host_epoch(None, 0, 0) == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_graph_replay(None, 0) == kvpub.KVPUB_ERR_INVALID_ARG
     assert kvpub.kvpub_graph_destroy(None) == kvpub.KVPUB_OK
     assert kvpub.kvpub_destroy(None) == kvpub.KVPUB_OK
@@ -120,7 +121,7 @@ def _cfg(**kw):
     ("num_lanes", 0), ("num_lanes", 65),
     ("num_participants", 0), ("num_participants", 9),
     ("device", -1),
-    ("flags", 1),                                        # reserved
+    ("flags", 2), ("flags", 0x80000001),                 # bits other than the acquire-wait option
 ])
 def test_create_rejects_each_bad_config_field(field, value):
     """Every configuration rule is checked on the host before any HIP call."""

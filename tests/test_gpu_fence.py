@@ -227,7 +227,7 @@ def test_create_rejects_bad_config():
         for field, val in (("num_replicas", 0), ("num_replicas", 9), ("block_size", 32),
                            ("main_page_stride", 41983), ("idx_page_stride", 8440),
                            ("main_layer_stride", 3 * 41984), ("num_lanes", 0),
-                           ("num_lanes", 65), ("num_participants", 9), ("flags", 1),
+                           ("num_lanes", 65), ("num_participants", 9), ("flags", 2),
                            ("struct_size", 8)):
             cfg = dev.config()
             setattr(cfg, field, val)
@@ -390,4 +390,114 @@ def test_graph_replays_wait_for_a_host_peer_at_each_epoch(orc):
     finally:
         if graph is not None:
             kvpub.kvpub_graph_destroy(graph)
+        dev.free()
+
+
+def _layered_inputs(seed, layers, T, capacity):
+    """Per-layer N(0,1) rows sharing one slot mapping of T distinct slots (a few padded)."""
+    rng = np.random.default_rng(seed)
+    slots = rng.choice(capacity, size=T, replace=False).astype(np.int64)
+    slots[rng.choice(T, size=T // 50, replace=False)] = -1
+    xs = []
+    for _ in range(layers):
+        lat = W.bf16_bits(rng.standard_normal((T, 512), dtype=np.float32))
+        rp = W.bf16_bits(rng.standard_normal((T, 64), dtype=np.float32))
+        ix = W.bf16_bits(rng.standard_normal((T, 128), dtype=np.float32))
+        xs.append(W.LayerInputs(lat, rp, ix, slots))
+    return xs
+
+
+def test_acquire_wait_fence_eager_and_replayed(orc):
+    """The one-participant fence with the acquire-wait option: eager fences and a
+    replayed store + fence graph advance the epoch once per fence, and the stores
+    are the oracle's bytes."""
+    import torch
+    layout = CacheLayout(replicas=2, layers=6, num_pages=64)
+    xs = _layered_inputs(31, layout.layers, 3000, layout.capacity)
+    dev = G.DeviceCache(layout, create=False)
+    graph = None
+    try:
+        cfg = dev.config()
+        cfg.flags = kvpub.KVPUB_CONFIG_FENCE_ACQUIRE_WAIT
+        st, dev.ctx = kvpub.kvpub_create(cfg, [b.data_ptr() for b in dev.main], [b.data_ptr() for b in dev.idx])
+        kvpub.check(st, "kvpub_create (acquire wait)")
+        G.log("acquire-wait fence: 5 eager fences, then 6 layers x T=3000 R=2 captured, 40 replays")
+        for _ in range(5):
+            kvpub.check(dev.fence(0))
+        assert dev.epoch(0) == 5
+        dxs = [G.DeviceInputs(x) for x in xs]
+        ios = [kvpub.layer_io(d.latent.data_ptr(), d.rope.data_ptr(), d.indexer.data_ptr(),
+                              d.slots.data_ptr(), d.T, l) for l, d in enumerate(dxs)]
+        st, graph = kvpub.kvpub_graph_create(dev.ctx, ios, 0)
+        kvpub.check(st, "kvpub_graph_create")
+        s = torch.cuda.current_stream().cuda_stream
+        for _ in range(40):
+            kvpub.check(kvpub.kvpub_graph_replay(graph, s))
+        assert dev.epoch(0) == orc.epoch_after(5, 40 * layout.layers)
+        st, invalid, flags = dev.errors()
+        assert st == kvpub.KVPUB_OK and invalid == 0 and flags == 0
+        mains, idxs, _ = G.oracle_replicas(orc, layout, list(enumerate(xs)))
+        G.assert_full_parity(dev, mains, idxs)
+    finally:
+        if graph is not None:
+            kvpub.kvpub_graph_destroy(graph)
+        dev.free()
+
+
+def test_host_epoch_fence_does_not_advance_under_replay(orc):
+    """The pages' two-launch fence with a host-held epoch (lane 0) beside the
+    single-launch device-epoch fence (lane 1), each captured after the same
+    stores: eagerly both count every fence; replayed, lane 1 advances by the
+    layer count on every replay while lane 0 stays at the value published at
+    capture.  Both graphs leave the oracle's bytes."""
+    import torch
+    layout = CacheLayout(replicas=2, layers=4, num_pages=32)
+    xs = _layered_inputs(32, layout.layers, 1500, layout.capacity)
+    dev = G.DeviceCache(layout, lanes=2)
+    try:
+        G.log("host-epoch fence: 3 eager, then 4 layers captured with each fence, 10 replays each")
+        for _ in range(3):
+            kvpub.check(kvpub.kvpub_fence_host_epoch(dev.ctx, 0, torch.cuda.current_stream().cuda_stream))
+            kvpub.check(dev.fence(1))
+        assert (dev.epoch(0), dev.epoch(1)) == (3, 3)
+        dxs = [G.DeviceInputs(x) for x in xs]
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        graphs = []
+        for lane in (0, 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for l, d in enumerate(dxs):
+                        kvpub.check(dev.store(l, d, stream=s), "kvpub_store (capture)")
+                        if lane == 0:
+                            kvpub.check(kvpub.kvpub_fence_host_epoch(dev.ctx, 0, s.cuda_stream))
+                        else:
+                            kvpub.check(dev.fence(1, stream=s))
+            graphs.append(g)
+        torch.cuda.synchronize()
+        assert (dev.epoch(0), dev.epoch(1)) == (3, 3), "capturing must not execute anything"
+        n = layout.layers
+        for rep in range(10):
+            graphs[0].replay()
+            graphs[1].replay()
+            torch.cuda.synchronize()
+            assert dev.epoch(0) == 3 + n, f"replay {rep}: the host-held epoch moved ({dev.epoch(0)})"
+            assert dev.epoch(1) == orc.epoch_after(3, n * (rep + 1)), f"replay {rep}: device epoch"
+        st, invalid, flags = dev.errors()
+        assert st == kvpub.KVPUB_OK and invalid == 0 and flags == 0
+        mains, idxs, _ = G.oracle_replicas(orc, layout, list(enumerate(xs)))
+        G.assert_full_parity(dev, mains, idxs)
+        del graphs
+    finally:
+        dev.free()
+
+
+def test_host_epoch_fence_needs_one_participant():
+    layout = CacheLayout(replicas=1, layers=1, num_pages=1)
+    dev = G.DeviceCache(layout, participants=2)
+    try:
+        assert kvpub.kvpub_fence_host_epoch(dev.ctx, 0, 0) == kvpub.KVPUB_ERR_UNSUPPORTED
+        assert kvpub.kvpub_fence_host_epoch(dev.ctx, 1, 0) == kvpub.KVPUB_ERR_INVALID_ARG
+    finally:
         dev.free()
