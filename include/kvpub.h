@@ -127,7 +127,7 @@ typedef struct {
     uint32_t num_participants;  /* fence participants, 1..8; > 1 only with host-driven peers (tests) */
     uint64_t fence_timeout_ns;  /* 0 = 5 s */
     int32_t device;             /* HIP device ordinal */
-    uint32_t flags;             /* 0 or KVPUB_CONFIG_FENCE_ACQUIRE_WAIT; other bits must be 0 */
+    uint32_t flags;             /* 0 or KVPUB_CONFIG_FENCE_RELEASE_ONLY; other bits must be 0 */
 } kvpub_config;
 
 /* With L == 1 the layer strides address nothing and are not checked; a value
@@ -136,15 +136,17 @@ typedef struct {
  * the bound of their write-through buffer range.  Any value is safe: no store
  * goes beyond the context's capacity. */
 
-/* kvpub_config.flags: with one participant, kvpub_fence follows its release
- * RMW with acquire loads of the lane's epoch until it holds the value the RMW
- * produced -- the system-scope release/acquire pair of vLLM PR #52863, Design
- * (device-epoch barrier), taken literally.  Without the flag a one-participant
- * fence is the release RMW alone (no other agent publishes into this GPU's
- * memory, and work after the fence runs in later kernels, which the queue
- * orders with its own acquire at dispatch).  No effect with peers: their fence
+/* kvpub_config.flags: with one participant, kvpub_fence is by default the
+ * system-scope release RMW of the lane's epoch followed by acquire loads of the
+ * epoch until it holds the value the RMW produced (with one participant the
+ * epoch is the only signal) -- the release/acquire pair of vLLM PR #52863,
+ * Design (device-epoch barrier).  With this flag it is the release RMW alone:
+ * no other agent publishes into this GPU's memory, and work after the fence
+ * runs in later kernels, which the queue orders with its own acquire at
+ * dispatch, so the acquire half has nothing to act on; it saves the system-
+ * scope cache invalidation of the acquire.  No effect with peers: their fence
  * always acquire-waits. */
-#define KVPUB_CONFIG_FENCE_ACQUIRE_WAIT 0x1u
+#define KVPUB_CONFIG_FENCE_RELEASE_ONLY 0x1u
 
 /* Fill *cfg with defaults for R replicas of L layers of num_pages dense pages:
  * page strides 41984 / 8448, layer strides num_pages * page stride, one lane,
@@ -254,16 +256,17 @@ KVPUB_API kvpub_status kvpub_vmm_destroy(kvpub_vmm *vmm);
 /* One fence on `lane`, asynchronously on `stream`: a single one-wavefront
  * kernel that adds 1 to the lane's device epoch with a system-scope
  * read-modify-write that releases every write made on this GPU before the
- * fence.  With one participant that release RMW is the whole fence (no other
- * agent publishes into this GPU's memory; work after the fence runs in later
- * kernels, ordered by their own acquire at dispatch).  With peers the RMW
- * also acquires, then the kernel publishes the new value as this
- * participant's signal and acquire-waits until every other participant's
+ * fence.  With one participant it then acquire-loads the epoch until it holds
+ * the new value (KVPUB_CONFIG_FENCE_RELEASE_ONLY: the release RMW alone).
+ * With peers the RMW also acquires, then the kernel publishes the new value as
+ * this participant's signal and acquire-waits until every other participant's
  * signal has reached it.  The expected value is never a kernel argument, so a captured
  * fence advances the epoch on every replay.  If the wait exceeds
  * fence_timeout_ns the kernel records KVPUB_FLAG_FENCE_TIMEOUT |
  * KVPUB_FLAG_POISONED and returns; from then on stores and fences of this
- * context write nothing (fail-closed; only a fence with peers can time out).
+ * context write nothing (fail-closed; with one participant the wait can only
+ * time out if the epoch was moved back, by kvpub_fence_host_epoch on the same
+ * lane).
  * No allocation and no synchronization: safe under stream capture. */
 KVPUB_API kvpub_status kvpub_fence(kvpub_ctx *ctx, uint32_t lane, kvpub_stream_t stream);
 

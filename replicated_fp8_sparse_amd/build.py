@@ -1,4 +1,5 @@
-"""Build libkvpub.so (the C-ABI library and its gfx950 kernels) in-tree with hipcc."""
+"""Build libkvpub.so (the C-ABI library and its gfx950 kernels) in-tree with hipcc,
+and libkvpub_floor.so (the plain-stream floor kernel the benchmark times beside it)."""
 import os
 import shutil
 import subprocess
@@ -10,6 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvpub.so")
 SOURCES = ["kvpub_api.hip", "store_kernel.hip", "fence_kernel.hip", "gather_kernel.hip", "vmm.hip"]
+FLOOR_LIB = os.path.join(PKG, "libkvpub_floor.so")
+FLOOR_SOURCES = ["floor_kernel.hip"]
 ARCH = "gfx950"
 
 # No fast-math, no FP contraction (explicit fmaf only); packed-fp32 instructions
@@ -30,8 +33,9 @@ def hipcc():
     return exe
 
 
-def build_library(out=LIB, extra_flags=()):
+def build_library(out=LIB, extra_flags=(), sources=None):
     """Compile every HIP source and link the shared library.  Always rebuilds."""
+    sources = SOURCES if sources is None else sources
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
@@ -44,8 +48,8 @@ def build_library(out=LIB, extra_flags=()):
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(max_workers=len(sources)) as ex:
+        objs = list(ex.map(compile_one, sources))
     tmp = out + ".tmp"
     r = subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
@@ -55,5 +59,14 @@ def build_library(out=LIB, extra_flags=()):
     return out
 
 
+def build_floor_library(out=FLOOR_LIB):
+    """The measurement-only floor kernel library.  Always rebuilds."""
+    return build_library(out, sources=FLOOR_SOURCES)
+
+
+def build_all():
+    return build_library(), build_floor_library()
+
+
 if __name__ == "__main__":
-    print(build_library())
+    print(build_all())

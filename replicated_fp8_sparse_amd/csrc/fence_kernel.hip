@@ -16,10 +16,11 @@
 //       visible after);
 //   with peers only: signal[self] = e (a release store), then for every
 //       other participant q: acquire-load signal[q] until it is >= e.
-// Alone (one participant) the release RMW is the whole fence by default; a
-// context created with the acquire-wait option follows it with acquire loads
-// of the epoch itself until it is >= e (with one participant the epoch is the
-// only signal), the release/acquire pair the Design section describes.
+// Alone (one participant) the release RMW is followed by acquire loads of the
+// epoch itself until it is >= e (with one participant the epoch is the only
+// signal): the release/acquire pair of PR #52863's Design section.  A context
+// created with the release-only option skips the acquire half, which has
+// nothing to act on alone (see fence_kernel).
 // This GPU's own signal is never awaited: it was written just before, in
 // program order, by the same wave.  The expected value e is read from device
 // memory, never passed as a kernel argument, so replaying a captured launch
@@ -58,21 +59,21 @@ __global__ __launch_bounds__(64) void fence_kernel(uint64_t* epoch, uint64_t* si
         // value this fence moved it to.  The RMW's result already shows that
         // value, so the first load passes unless the epoch was moved back (by a
         // host-epoch fence on the same lane); the wait is bounded all the same.
+        // No status check first: only a wait can poison, and one that follows
+        // this wave's own RMW does not time out in normal use.
         const uint64_t e =
             __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM) + 1;
         (void)wait_at_least(epoch, e, status, wall_clock64(), timeout_ticks);
         return;
     }
     if (num_participants == 1) {
-        // Alone, the epoch is the whole barrier: a release RMW at system scope
-        // publishes every write this GPU made before the fence, then the epoch
-        // moves.  The acquire half has nothing to act on: no other agent
-        // publishes into this GPU's memory, and this wave ends right after the
-        // RMW, so work after the fence runs in later kernels, which are ordered
-        // by their own acquire at dispatch (an acquire here would only
-        // invalidate the L2 for them).  Only a fence waiting for peers can time
-        // out and poison the context, so there is no status to check first (one
-        // memory round trip) and no signal for anyone to read.
+        // The release-only option: a release RMW at system scope publishes
+        // every write this GPU made before the fence, then the epoch moves, and
+        // nothing more.  The acquire half has nothing to act on alone: no other
+        // agent publishes into this GPU's memory, and this wave ends right after
+        // the RMW, so work after the fence runs in later kernels, which are
+        // ordered by their own acquire at dispatch (an acquire here would only
+        // invalidate the L2 for them).
         __hip_atomic_fetch_add(epoch, (uint64_t)1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         return;
     }

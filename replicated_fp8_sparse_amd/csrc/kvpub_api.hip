@@ -108,7 +108,7 @@ kvpub_status check_config(const kvpub_config* c) {
     }
     if (c->num_lanes < 1 || c->num_lanes > KVPUB_MAX_LANES) return KVPUB_ERR_INVALID_ARG;
     if (c->num_participants < 1 || c->num_participants > KVPUB_MAX_PARTICIPANTS) return KVPUB_ERR_INVALID_ARG;
-    if (c->device < 0 || (c->flags & ~KVPUB_CONFIG_FENCE_ACQUIRE_WAIT) != 0) return KVPUB_ERR_INVALID_ARG;
+    if (c->device < 0 || (c->flags & ~KVPUB_CONFIG_FENCE_RELEASE_ONLY) != 0) return KVPUB_ERR_INVALID_ARG;
     return KVPUB_OK;
 }
 
@@ -173,7 +173,7 @@ FenceParams fence_params(kvpub_ctx* ctx, uint32_t lane) {
     f.self = 0;
     f.status = reinterpret_cast<uint32_t*>(ctx->words + kvpub::kStatusOffset);
     f.timeout_ticks = ctx->timeout_ticks;
-    f.acquire_wait = (ctx->cfg.flags & KVPUB_CONFIG_FENCE_ACQUIRE_WAIT) ? 1u : 0u;
+    f.acquire_wait = (ctx->cfg.flags & KVPUB_CONFIG_FENCE_RELEASE_ONLY) ? 0u : 1u;
     return f;
 }
 
@@ -187,6 +187,18 @@ void release(kvpub_ctx* c) {
 
 kvpub_status sync_device() {
     return map_hip(hipDeviceSynchronize());
+}
+
+// Timeout in wall-clock (s_memrealtime) ticks for a context on `device`.
+hipError_t timeout_ticks_for(const kvpub_config* cfg, uint64_t* out) {
+    int khz = 0;
+    const hipError_t e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, cfg->device);
+    if (e != hipSuccess) return e;
+    if (khz <= 0) return hipErrorInvalidValue;
+    const uint64_t ns = cfg->fence_timeout_ns ? cfg->fence_timeout_ns : kDefaultTimeoutNs;
+    *out = (uint64_t)((double)ns * (double)khz / 1.0e6);
+    if (*out == 0) *out = 1;
+    return hipSuccess;
 }
 
 }  // namespace
@@ -296,12 +308,7 @@ KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_b
                            : hipStreamCreateWithFlags(&c->capture_stream, hipStreamNonBlocking);
     if (e != hipSuccess) { c->capture_stream = nullptr; release(c); return map_hip(e); }
 
-    int khz = 0;
-    e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, cfg->device);
-    if (e != hipSuccess || khz <= 0) { release(c); return KVPUB_ERR_HIP; }
-    const uint64_t ns = cfg->fence_timeout_ns ? cfg->fence_timeout_ns : kDefaultTimeoutNs;
-    c->timeout_ticks = (uint64_t)((double)ns * (double)khz / 1.0e6);
-    if (c->timeout_ticks == 0) c->timeout_ticks = 1;
+    if (timeout_ticks_for(cfg, &c->timeout_ticks) != hipSuccess) { release(c); return KVPUB_ERR_HIP; }
 
     *out = c;
     return KVPUB_OK;

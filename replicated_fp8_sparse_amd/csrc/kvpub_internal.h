@@ -62,7 +62,7 @@ struct FenceParams {
     uint32_t self;               // this GPU's participant index (0)
     uint32_t* status;
     uint64_t timeout_ticks;      // in wall-clock (s_memrealtime) ticks
-    uint32_t acquire_wait;       // alone: acquire-wait on the epoch after the release RMW
+    uint32_t acquire_wait;       // alone: acquire-wait on the epoch after the release RMW (else release only)
 };
 
 // Enqueue one store kernel on `stream`; returns the launch status.

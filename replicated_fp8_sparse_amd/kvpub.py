@@ -27,7 +27,7 @@ KVPUB_ERR_FENCE_TIMEOUT = 6
 KVPUB_FLAG_FENCE_TIMEOUT = 0x1
 KVPUB_FLAG_POISONED = 0x2
 
-KVPUB_CONFIG_FENCE_ACQUIRE_WAIT = 0x1
+KVPUB_CONFIG_FENCE_RELEASE_ONLY = 0x1
 
 SLOTS_PER_PAGE = 64
 LATENT_DIM = 512

@@ -121,7 +121,7 @@ def _cfg(**kw):
     ("num_lanes", 0), ("num_lanes", 65),
     ("num_participants", 0), ("num_participants", 9),
     ("device", -1),
-    ("flags", 2), ("flags", 0x80000001),                 # bits other than the acquire-wait option
+    ("flags", 2), ("flags", 0x80000001),                 # bits other than the release-only option
 ])
 def test_create_rejects_each_bad_config_field(field, value):
     """Every configuration rule is checked on the host before any HIP call."""
@@ -163,3 +163,27 @@ def test_the_abi_from_plain_c(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+FLOOR_HEADER = os.path.join(ROOT, "include", "kvpub_floor.h")
+
+
+def test_floor_library_exports_its_header():
+    """The benchmark's floor-kernel library exports what include/kvpub_floor.h declares
+    and rejects bad arguments on the host (nothing launched)."""
+    from replicated_fp8_sparse_amd import build, floor
+    if not os.path.exists(floor.LIB_PATH):
+        build.build_floor_library()
+    declared = sorted(set(re.findall(r"KVPUB_FLOOR_API\s+[\w\s\*]+?\b(kvpub_\w+)\s*\(", open(FLOOR_HEADER).read())))
+    assert declared == sorted(floor.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", floor.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(re.findall(r"\bT (kvpub_\w+)", out)) == set(declared)
+    f = floor.kvpub_floor_stream
+    assert f(0, 16, [16], 16, 0) == 1                      # null input
+    assert f(16, 16, [], 16, 0) == 1                       # no output
+    assert f(16, 16, [16] * 9, 16, 0) == 1                 # more than 8 outputs
+    assert f(16, 24, [16], 16, 0) == 1                     # not a multiple of 16
+    assert f(8, 16, [16], 16, 0) == 1                      # misaligned
+    assert f(16, 16, [16], 16, 3) == 1                     # unknown policy
+    assert f(16, 16, [16], 1 << 32, floor.KVPUB_FLOOR_WRITE_THROUGH) == 1   # 32-bit buffer offsets

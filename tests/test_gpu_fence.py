@@ -407,8 +407,8 @@ def _layered_inputs(seed, layers, T, capacity):
     return xs
 
 
-def test_acquire_wait_fence_eager_and_replayed(orc):
-    """The one-participant fence with the acquire-wait option: eager fences and a
+def test_release_only_fence_eager_and_replayed(orc):
+    """The one-participant fence with the release-only option: eager fences and a
     replayed store + fence graph advance the epoch once per fence, and the stores
     are the oracle's bytes."""
     import torch
@@ -418,10 +418,10 @@ def test_acquire_wait_fence_eager_and_replayed(orc):
     graph = None
     try:
         cfg = dev.config()
-        cfg.flags = kvpub.KVPUB_CONFIG_FENCE_ACQUIRE_WAIT
+        cfg.flags = kvpub.KVPUB_CONFIG_FENCE_RELEASE_ONLY
         st, dev.ctx = kvpub.kvpub_create(cfg, [b.data_ptr() for b in dev.main], [b.data_ptr() for b in dev.idx])
-        kvpub.check(st, "kvpub_create (acquire wait)")
-        G.log("acquire-wait fence: 5 eager fences, then 6 layers x T=3000 R=2 captured, 40 replays")
+        kvpub.check(st, "kvpub_create (release only)")
+        G.log("release-only fence: 5 eager fences, then 6 layers x T=3000 R=2 captured, 40 replays")
         for _ in range(5):
             kvpub.check(dev.fence(0))
         assert dev.epoch(0) == 5
