@@ -105,6 +105,7 @@ typedef enum {
     KVPUB_ERR_HIP = 4,           /* a HIP runtime call failed */
     KVPUB_ERR_CAPTURING = 5,     /* a synchronizing call while a stream capture is active */
     KVPUB_ERR_FENCE_TIMEOUT = 6, /* a fence timed out: the context is poisoned */
+    KVPUB_ERR_IN_USE = 7,        /* the device's static context (kvpub_create_static) is in use */
     KVPUB_STATUS_MAX_ENUM = 0x7FFFFFFF /* not a status: makes every non-negative int32 a valid
                                           kvpub_status value, so a C caller may pass any code */
 } kvpub_status;
@@ -164,6 +165,28 @@ KVPUB_API void kvpub_config_init(kvpub_config *cfg, uint32_t num_replicas, uint3
  * is set to NULL.  Returns KVPUB_ERR_UNSUPPORTED unless the device is gfx950. */
 KVPUB_API kvpub_status kvpub_create(const kvpub_config *cfg, void *const *main_bases,
                           void *const *idx_bases, kvpub_ctx **out);
+
+/* kvpub_create for callers that cannot allocate: code that must not call
+ * hipMalloc or any other allocator (tight serving loops, harnesses that forbid
+ * allocation).  Same configuration rules, bases and behaviour as kvpub_create,
+ * and the context is used and destroyed the same way (kvpub_destroy), but this
+ * call allocates nothing, host or device: the context's device words (status
+ * and capacity, invalid-slot counter, one epoch per lane) live in a fixed
+ * 8448-byte array of the library's, one per GPU, held until the process ends,
+ * and its host part in static storage.  The words are cleared and the capacity
+ * written by a kernel enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream): work on the context must follow it on that stream or after it.
+ * Limits: one participant (peers' signals need host memory:
+ * KVPUB_ERR_UNSUPPORTED), device ordinal < 64, and one static context per GPU
+ * at a time -- a second call while one is alive returns KVPUB_ERR_IN_USE.
+ * Every static context on a GPU uses that GPU's one array, so calls on it that
+ * overlap (another thread creating a static context the moment this one is
+ * destroyed, while kernels of the old one still run on another stream) race;
+ * kvpub_destroy synchronizes the device first.  Not during stream capture of
+ * `stream` (KVPUB_ERR_CAPTURING).  kvpub_graph_create on such a context
+ * captures on a temporary stream (creating the graph allocates, as always). */
+KVPUB_API kvpub_status kvpub_create_static(const kvpub_config *cfg, void *const *main_bases,
+                                           void *const *idx_bases, kvpub_stream_t stream, kvpub_ctx **out);
 
 /* Quantize num_tokens tokens' final rows and write them into every replica's
  * layer `layer`, asynchronously on `stream`.

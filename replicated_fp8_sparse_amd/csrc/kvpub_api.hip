@@ -7,6 +7,7 @@
 #include <cstddef>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "kvpub.h"
@@ -25,6 +26,7 @@ struct kvpub_ctx {
     uint64_t timeout_ticks;
     hipStream_t capture_stream;
     uint64_t host_epoch[KVPUB_MAX_LANES];   // kvpub_fence_host_epoch: the epoch each lane last published
+    bool is_static;            // kvpub_create_static: words in the static array, this struct in static storage
 };
 
 struct kvpub_graph {
@@ -177,8 +179,11 @@ FenceParams fence_params(kvpub_ctx* ctx, uint32_t lane) {
     return f;
 }
 
+void release_static(kvpub_ctx* c);
+
 void release(kvpub_ctx* c) {
     if (!c) return;
+    if (c->is_static) { release_static(c); return; }
     if (c->capture_stream) (void)hipStreamDestroy(c->capture_stream);
     if (c->host_signals) (void)hipHostFree(c->host_signals);
     if (c->words) (void)hipFree(c->words);
@@ -198,6 +203,65 @@ hipError_t timeout_ticks_for(const kvpub_config* cfg, uint64_t* out) {
     const uint64_t ns = cfg->fence_timeout_ns ? cfg->fence_timeout_ns : kDefaultTimeoutNs;
     *out = (uint64_t)((double)ns * (double)khz / 1.0e6);
     if (*out == 0) *out = 1;
+    return hipSuccess;
+}
+
+// ---- contexts that allocate nothing (kvpub_create_static) -------------------
+//
+// Their device words live in `scratch`, a file-scope device array of fixed
+// size: the status line, the invalid-slot counter and the epochs of the
+// largest lane count.  Each GPU holds its own copy for the life of the
+// process.  In host code `scratch` names a host-side stand-in, not the device
+// memory: the device address comes from hipGetSymbolAddress, resolved once per
+// device with that device current, and only that address is used.  The host
+// part of the context is one static struct per device.  One static context
+// per device at a time: its words are that device's array.
+constexpr size_t kStaticWordsBytes = kvpub::kEpochOffset + (size_t)KVPUB_MAX_LANES * kvpub::kLine;  // 8448
+constexpr int kMaxStaticDevices = 64;
+
+struct StaticSlot {
+    uint8_t* words;   // device address of this device's `scratch`
+    bool in_use;
+    kvpub_ctx ctx;
+};
+StaticSlot g_static[kMaxStaticDevices];
+std::mutex g_static_mu;
+
+void release_static(kvpub_ctx* c) {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    g_static[c->cfg.device].in_use = false;
+}
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticWordsBytes];
+
+namespace {
+
+// Clears a static context's words (status, counter, every lane's epoch) and
+// writes the capacity: one block, 16-byte vector stores.
+__global__ __launch_bounds__(256) void init_words_kernel(uint8_t* words, uint32_t bytes, int64_t capacity) {
+    for (uint32_t i = threadIdx.x * 16u; i < bytes; i += blockDim.x * 16u) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (i == 0) {   // the CtxHead line starts with {status, reserved, capacity}
+            v.z = (uint32_t)((uint64_t)capacity & 0xFFFFFFFFu);
+            v.w = (uint32_t)((uint64_t)capacity >> 32);
+        }
+        *reinterpret_cast<uint4*>(words + i) = v;
+    }
+}
+
+// The device address of this device's `scratch` (the device must be current).
+hipError_t static_words(int device, uint8_t** out) {
+    StaticSlot& slot = g_static[device];
+    if (!slot.words) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        slot.words = static_cast<uint8_t*>(ptr);
+    }
+    *out = slot.words;
     return hipSuccess;
 }
 
@@ -314,6 +378,64 @@ KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_b
     return KVPUB_OK;
 }
 
+KVPUB_API kvpub_status kvpub_create_static(const kvpub_config* cfg, void* const* main_bases,
+                                          void* const* idx_bases, kvpub_stream_t stream, kvpub_ctx** out) {
+    if (!out) return KVPUB_ERR_INVALID_ARG;
+    *out = nullptr;
+    kvpub_status st = check_config(cfg);
+    if (st != KVPUB_OK) return st;
+    if (!main_bases || !idx_bases) return KVPUB_ERR_INVALID_ARG;
+    for (uint32_t r = 0; r < cfg->num_replicas; ++r) {
+        if (!main_bases[r] || !idx_bases[r]) return KVPUB_ERR_INVALID_ARG;
+        if (!aligned(main_bases[r], 16) || !aligned(idx_bases[r], 16)) return KVPUB_ERR_INVALID_ARG;
+    }
+    // host-driven peers' signals would need host memory of their own
+    if (cfg->num_participants != 1) return KVPUB_ERR_UNSUPPORTED;
+    if (kvpub::kEpochOffset + (size_t)cfg->num_lanes * kvpub::kLine > kStaticWordsBytes) return KVPUB_ERR_INVALID_ARG;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return KVPUB_ERR_HIP;
+    if (cfg->device >= ndev) return KVPUB_ERR_INVALID_ARG;
+    if (cfg->device >= kMaxStaticDevices) return KVPUB_ERR_UNSUPPORTED;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, cfg->device) != hipSuccess) return KVPUB_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return KVPUB_ERR_UNSUPPORTED;
+
+    DeviceGuard guard(cfg->device);
+    if (!guard.ok) return KVPUB_ERR_HIP;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess) return KVPUB_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return KVPUB_ERR_CAPTURING;
+    uint64_t ticks = 0;
+    if (timeout_ticks_for(cfg, &ticks) != hipSuccess) return KVPUB_ERR_HIP;
+
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticSlot& slot = g_static[cfg->device];
+    if (slot.in_use) return KVPUB_ERR_IN_USE;
+    uint8_t* words = nullptr;
+    hipError_t e = static_words(cfg->device, &words);
+    if (e != hipSuccess) return map_hip(e);
+
+    (void)hipGetLastError();
+    init_words_kernel<<<dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+        words, (uint32_t)kStaticWordsBytes, (int64_t)(cfg->num_pages * KVPUB_SLOTS_PER_PAGE));
+    e = hipGetLastError();
+    if (e != hipSuccess) return map_hip(e);
+
+    kvpub_ctx* c = &slot.ctx;
+    std::memset(c, 0, sizeof *c);
+    c->cfg = *cfg;
+    for (uint32_t r = 0; r < cfg->num_replicas; ++r) {
+        c->main_base[r] = static_cast<uint8_t*>(main_bases[r]);
+        c->idx_base[r] = static_cast<uint8_t*>(idx_bases[r]);
+    }
+    c->words = words;
+    c->timeout_ticks = ticks;
+    c->is_static = true;
+    slot.in_use = true;
+    *out = c;
+    return KVPUB_OK;
+}
+
 KVPUB_API kvpub_status kvpub_store(kvpub_ctx* ctx, uint32_t layer, int64_t num_tokens,
                                   const void* latent, int64_t latent_row_stride, const void* rope,
                                   int64_t rope_row_stride, const void* indexer,
@@ -407,7 +529,19 @@ KVPUB_API kvpub_status kvpub_graph_create(kvpub_ctx* ctx, const kvpub_layer_io* 
     g->graph = nullptr;
     g->exec = nullptr;
 
+    // A context from kvpub_create_static has no stream of its own: capture on
+    // a temporary one.
     hipStream_t s = ctx->capture_stream;
+    hipStream_t temp = nullptr;
+    if (!s) {
+        const hipError_t ce = hipStreamCreateWithFlags(&temp, hipStreamNonBlocking);
+        if (ce != hipSuccess) { delete g; return map_hip(ce); }
+        s = temp;
+    }
+    struct TempStream {
+        hipStream_t s;
+        ~TempStream() { if (s) (void)hipStreamDestroy(s); }
+    } temp_guard{temp};
     hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) { delete g; return map_hip(e); }
     hipError_t launch_err = hipSuccess;
@@ -516,6 +650,7 @@ KVPUB_API const char* kvpub_strerror(kvpub_status s) {
         case KVPUB_ERR_HIP: return "HIP runtime error";
         case KVPUB_ERR_CAPTURING: return "synchronizing call during stream capture";
         case KVPUB_ERR_FENCE_TIMEOUT: return "fence timed out; context poisoned";
+        case KVPUB_ERR_IN_USE: return "the device's static context is in use";
         case KVPUB_STATUS_MAX_ENUM: break;
     }
     return "unknown status";

@@ -23,6 +23,7 @@ KVPUB_ERR_UNSUPPORTED = 3
 KVPUB_ERR_HIP = 4
 KVPUB_ERR_CAPTURING = 5
 KVPUB_ERR_FENCE_TIMEOUT = 6
+KVPUB_ERR_IN_USE = 7
 
 KVPUB_FLAG_FENCE_TIMEOUT = 0x1
 KVPUB_FLAG_POISONED = 0x2
@@ -40,7 +41,7 @@ IDX_SCALES_OFFSET = 64 * 128
 MAX_REPLICAS = 8
 
 # Every function include/kvpub.h declares.
-EXPORTS = ("kvpub_config_init", "kvpub_create", "kvpub_store", "kvpub_gather", "kvpub_fence",
+EXPORTS = ("kvpub_config_init", "kvpub_create", "kvpub_create_static", "kvpub_store", "kvpub_gather", "kvpub_fence",
            "kvpub_fence_host_epoch",
            "kvpub_graph_create", "kvpub_graph_replay", "kvpub_graph_destroy",
            "kvpub_epoch_read", "kvpub_error_read", "kvpub_participant_signal",
@@ -102,6 +103,7 @@ def load(path=LIB_PATH):
     sig = {
         "kvpub_config_init": (None, [cfgp, u32, u32, u64]),
         "kvpub_create": (i32, [cfgp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp)]),
+        "kvpub_create_static": (i32, [cfgp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, ctypes.POINTER(vp)]),
         "kvpub_store": (i32, [vp, u32, i64, vp, i64, vp, i64, vp, i64, vp, vp]),
         "kvpub_gather": (i32, [vp, u32, u32, i64, vp, vp, i64, vp, i64, vp, i64, vp]),
         "kvpub_fence": (i32, [vp, u32, vp]),
@@ -156,6 +158,17 @@ def kvpub_create(cfg, main_bases, idx_bases):
     ib = (ctypes.c_void_p * R)(*idx_bases)
     out = ctypes.c_void_p()
     st = load().kvpub_create(ctypes.byref(cfg), mb, ib, ctypes.byref(out))
+    return st, (out.value if st == KVPUB_OK else None)
+
+
+def kvpub_create_static(cfg, main_bases, idx_bases, stream=0):
+    """Returns (status, ctx handle or None); the context's words live in the
+    library's static per-GPU array (no allocation)."""
+    R = len(main_bases)
+    mb = (ctypes.c_void_p * R)(*main_bases)
+    ib = (ctypes.c_void_p * R)(*idx_bases)
+    out = ctypes.c_void_p()
+    st = load().kvpub_create_static(ctypes.byref(cfg), mb, ib, stream, ctypes.byref(out))
     return st, (out.value if st == KVPUB_OK else None)
 
 
