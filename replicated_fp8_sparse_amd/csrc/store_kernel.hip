@@ -42,6 +42,8 @@
 // treat the L2 depends on the launch size (see put_at).  Batches of up to
 // about a thousand tokens take small_store_kernel instead, which spreads a
 // group's five rounds over five waves with the same per-tile arithmetic.
+#include <type_traits>
+
 #include "kvpub_internal.h"
 
 namespace kvpub {
@@ -89,8 +91,10 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data for
 constexpr int kDeviceCoherent = 16;      // buffer cache-policy bits: sc1
 
 // Store v at base + off: `whole` marks a piece of the whole-line kind (see above).
-template <bool NT, bool WT, bool whole, class T>
-__device__ __forceinline__ void put_at(gbyte* base, uint32_t region, uint64_t off, T v) {
+// With a 32-bit offset the address is a uniform base plus a 32-bit lane offset,
+// which the store instruction takes as is (no 64-bit address arithmetic).
+template <bool NT, bool WT, bool whole, class T, class O>
+__device__ __forceinline__ void put_at(gbyte* base, uint32_t region, O off, T v) {
     if constexpr (WT) {
         const __amdgpu_buffer_rsrc_t r =
             __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)region, kRsrcWord3);
@@ -272,31 +276,50 @@ struct Bases {
     gbyte* idx[R];
 };
 
+// Offsets within a replica's layer: 32-bit when every layer spans less than
+// 4 GiB (O32), else 64-bit.
+template <bool O32> using Off = typename std::conditional<O32, uint32_t, uint64_t>::type;
+
+template <bool O32>
 struct Dest {
-    uint64_t row[4];   // Main-KV row of token k (wave-uniform)
+    Off<O32> row[4];   // Main-KV row of token k (wave-uniform)
     uint32_t tok;      // bit k: token k is stored (wave-uniform)
-    uint64_t rope;     // this lane's RoPE piece (lanes 0..31)
-    uint64_t icode;    // this lane's Indexer-K code piece
-    uint64_t iscale;   // this lane's Indexer-K scale (all 16 lanes of a row)
+    Off<O32> rope;     // this lane's RoPE piece (lanes 0..31)
+    Off<O32> icode;    // this lane's Indexer-K code piece
+    Off<O32> iscale;   // this lane's Indexer-K scale (all 16 lanes of a row)
     uint32_t ok_r, ok_g;   // this lane's RoPE / Indexer-K token is stored
     uint32_t run;      // the 4 rows are consecutive slots of one page (wave-uniform)
 };
 
+// s is a slot of the cache: 0 <= s < capacity.  With 32-bit offsets the
+// capacity is below 2^32 (a layer spans less than 4 GiB and a page holds 64
+// slots in at least 41984 bytes), so the test splits into two 32-bit ones on
+// the slot's halves: scalar instructions (there is no 64-bit scalar less-than).
+template <bool O32>
 __device__ __forceinline__ bool slot_ok(int64_t s, int64_t capacity) {
-    return (uint64_t)s < (uint64_t)capacity;   // negative slots wrap to huge values
+    if constexpr (O32) {
+        // the halves pass through registers so that the two tests are not
+        // folded back into one 64-bit comparison (a vector instruction)
+        uint32_t hi = (uint32_t)((uint64_t)s >> 32), lo = (uint32_t)s;
+        asm volatile("" : "+s"(hi), "+s"(lo));
+        return (hi == 0u) & (lo < (uint32_t)capacity);
+    } else {
+        return (uint64_t)s < (uint64_t)capacity;   // negative slots wrap to huge values
+    }
 }
 
 // v_i for a per-lane index i in 0..3; v0..v3 wave-uniform.
-__device__ __forceinline__ uint64_t pick4(uint64_t v0, uint64_t v1, uint64_t v2, uint64_t v3, uint32_t i) {
-    const uint64_t a = (i & 1u) ? v1 : v0;
-    const uint64_t b = (i & 1u) ? v3 : v2;
+template <class O>
+__device__ __forceinline__ O pick4(O v0, O v1, O v2, O v3, uint32_t i) {
+    const O a = (i & 1u) ? v1 : v0;
+    const O b = (i & 1u) ? v3 : v2;
     return (i & 2u) ? b : a;
 }
 
 // The value is materialized in a register at this point, so later code
 // cannot pull its computation below (past the wait for the row data).
-__device__ __forceinline__ uint64_t pin_s(uint64_t v) { asm volatile("" : "+s"(v)); return v; }
-__device__ __forceinline__ uint64_t pin_v(uint64_t v) { asm volatile("" : "+v"(v)); return v; }
+template <class O> __device__ __forceinline__ O pin_s(O v) { asm volatile("" : "+s"(v)); return v; }
+template <class O> __device__ __forceinline__ O pin_v(O v) { asm volatile("" : "+v"(v)); return v; }
 __device__ __forceinline__ uint32_t pin_v32(uint32_t v) { asm volatile("" : "+v"(v)); return v; }
 __device__ __forceinline__ gbyte* pin_ptr(uint8_t* v) {
     gbyte* g = (gbyte*)v;
@@ -315,28 +338,48 @@ __device__ __forceinline__ Bases<R> pin_bases(const StoreParams& p) {
     return b;
 }
 
-__device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2, int64_t s3, bool poisoned,
-                                             int64_t capacity, uint32_t lane, const StoreParams& p) {
+// tok: bit k set if token k is stored (its slot is a slot of the cache and the
+// context is not poisoned; wave-uniform).
+template <bool O32>
+__device__ __forceinline__ Dest<O32> destinations(int64_t s0, int64_t s1, int64_t s2, int64_t s3, uint32_t tok,
+                                                  uint32_t lane, const StoreParams& p) {
+    using O = Off<O32>;
     const int64_t sl[4] = {s0, s1, s2, s3};
-    uint64_t row[4], irow[4], iscl[4];
-    uint32_t tok = 0;
+    O row[4], irow[4], iscl[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint64_t page = (uint64_t)sl[k] >> 6, in = (uint64_t)sl[k] & 63u;
-        row[k] = pin_s(page * p.main_page_stride + in * 656u);
-        irow[k] = page * p.idx_page_stride + in * 128u;
-        iscl[k] = page * p.idx_page_stride + 8192u + in * 4u;
-        tok |= (!poisoned && slot_ok(sl[k], capacity)) ? (1u << k) : 0u;
+        if constexpr (O32) {
+            // every offset of a slot that is stored fits in 32 bits; the
+            // offsets of skipped slots are never used
+            const uint32_t lo = (uint32_t)sl[k], page = lo >> 6, in = lo & 63u;
+            row[k] = pin_s(page * (uint32_t)p.main_page_stride + in * 656u);
+            const uint32_t ib = page * (uint32_t)p.idx_page_stride;
+            irow[k] = ib + in * 128u;
+            iscl[k] = ib + 8192u + in * 4u;
+        } else {
+            const uint64_t page = (uint64_t)sl[k] >> 6, in = (uint64_t)sl[k] & 63u;
+            row[k] = pin_s(page * p.main_page_stride + in * 656u);
+            irow[k] = page * p.idx_page_stride + in * 128u;
+            iscl[k] = page * p.idx_page_stride + 8192u + in * 4u;
+        }
     }
     const uint32_t g = lane >> 4, r = (lane >> 3) & 3u;
-    Dest d;
+    Dest<O32> d;
 #pragma unroll
     for (int k = 0; k < 4; ++k) d.row[k] = row[k];
     tok = __builtin_amdgcn_readfirstlane(tok);   // uniform; computed once, before the wait
     asm volatile("" : "+s"(tok));
     // the 4 rows are one contiguous run: all stored, consecutive slots of one page
-    uint32_t run = (tok == 0xFu && s1 == s0 + 1 && s2 == s0 + 2 && s3 == s0 + 3 && (s0 & 63) <= 60)
-                       ? 1u : 0u;
+    // (all four stored: with 32-bit offsets their high halves are zero)
+    bool consecutive;
+    if constexpr (O32) {
+        const uint32_t l0 = (uint32_t)s0;
+        consecutive = (uint32_t)s1 == l0 + 1u && (uint32_t)s2 == l0 + 2u && (uint32_t)s3 == l0 + 3u &&
+                      (l0 & 63u) <= 60u;
+    } else {
+        consecutive = s1 == s0 + 1 && s2 == s0 + 2 && s3 == s0 + 3 && (s0 & 63) <= 60;
+    }
+    uint32_t run = (tok == 0xFu && consecutive) ? 1u : 0u;
     run = __builtin_amdgcn_readfirstlane(run);
     asm volatile("" : "+s"(run));
     d.tok = tok;
@@ -357,8 +400,8 @@ __device__ __forceinline__ Dest destinations(int64_t s0, int64_t s1, int64_t s2,
 //   Indexer-K scale   -> page bytes [8192 + 4*(slot%64), +4) (lane 16g)
 // The five rounds are computed as one straight-line block (their reductions
 // and scale sequences interleave); only the stores are conditional.
-template <int R, bool NT, bool WT>
-__device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, const Bases<R>& b, uint32_t lane,
+template <int R, bool NT, bool WT, bool O32>
+__device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& d, const Bases<R>& b, uint32_t lane,
                                                lbyte* img, uint32_t main_region, uint32_t idx_region) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
@@ -436,7 +479,7 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest& d, co
         const u32x4 c2 = lane < 36u ? *(lptr<u32x4>)(img + 2048u + lane * 16u) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint64_t o = d.row[0] + lane * 16u;
+            const Off<O32> o = d.row[0] + lane * 16u;
             put_at<NT, WT, true>(b.main[r], main_region, o, c0);
             put_at<NT, WT, true>(b.main[r], main_region, o + 1024u, c1);
             if (lane < 36u) put_at<NT, WT, true>(b.main[r], main_region, o + 2048u, c2);
@@ -498,7 +541,7 @@ __device__ __forceinline__ void fetch_rows(const uint16_t* latent, const uint16_
 // instructions need: they arrive preloaded in SGPRs (kernel-argument
 // preloading); p is fetched while the row loads are in flight.  Token
 // indices are 32-bit (a launch holds at most kMaxTokensPerLaunch tokens).
-template <int R, bool NT, bool WT>
+template <int R, bool NT, bool WT, bool O32>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
@@ -522,17 +565,19 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const bool poisoned = (h.status & kStatusPoisoned) != 0;  // a fence timed out: fail closed
     // Slots of tokens past the end become -1; invalid slots (neither -1 nor a
     // slot of the cache) are skipped and counted.
-    uint32_t nbad = 0;
+    uint32_t ok = 0, pad = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         sl[k] = t0 + k <= last ? sl[k] : -1;
-        nbad += (sl[k] != -1 && !slot_ok(sl[k], h.capacity)) ? 1u : 0u;
+        ok |= slot_ok<O32>(sl[k], h.capacity) ? (1u << k) : 0u;
+        pad |= sl[k] == -1 ? (1u << k) : 0u;
     }
+    const uint32_t nbad = (uint32_t)__builtin_popcount(~(ok | pad) & 0xFu);
     if (nbad != 0 && !poisoned && lane == 0) atomicAdd(p.invalid_count, (unsigned long long)nbad);
     const Bases<R> b = pin_bases<R>(p);
-    const Dest d = destinations(sl[0], sl[1], sl[2], sl[3], poisoned, h.capacity, lane, p);
+    const Dest<O32> d = destinations<O32>(sl[0], sl[1], sl[2], sl[3], poisoned ? 0u : ok, lane, p);
     __builtin_amdgcn_sched_barrier(0);
-    quantize_store<R, NT, WT>(G, d, b, lane, (lbyte*)&run_img[wave][0], p.main_region, p.idx_region);
+    quantize_store<R, NT, WT, O32>(G, d, b, lane, (lbyte*)&run_img[wave][0], p.main_region, p.idx_region);
 }
 
 // Small batches (a decode step: tens of tokens; up to about a thousand).
@@ -571,7 +616,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         sl[k] = t0 + k <= last ? sl[k] : -1;
-        const bool good = slot_ok(sl[k], h.capacity);
+        const bool good = slot_ok<false>(sl[k], h.capacity);
         nbad += (sl[k] != -1 && !good) ? 1u : 0u;
         tok |= (!poisoned && good) ? (1u << k) : 0u;
     }
@@ -636,20 +681,20 @@ __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
 
 }  // namespace
 
-template <bool NT, bool WT>
+template <bool NT, bool WT, bool O32>
 static void launch_r(uint32_t num_replicas, dim3 grid, dim3 block, hipStream_t stream, const uint16_t* lat,
                      const uint16_t* rp, const uint16_t* ix, const int64_t* sl, uint32_t n, const StoreParams& p) {
 #define KVPUB_ROW_ARGS lat, rp, ix, sl, n, (uint32_t)p.latent_stride, (uint32_t)p.rope_stride, \
     (uint32_t)p.indexer_stride, p.head, p
     switch (num_replicas) {
-        case 1: store_kernel<1, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 2: store_kernel<2, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 3: store_kernel<3, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 4: store_kernel<4, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 5: store_kernel<5, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 6: store_kernel<6, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 7: store_kernel<7, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        default: store_kernel<8, NT, WT><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 1: store_kernel<1, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 2: store_kernel<2, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 3: store_kernel<3, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 4: store_kernel<4, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 5: store_kernel<5, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 6: store_kernel<6, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 7: store_kernel<7, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        default: store_kernel<8, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
     }
 #undef KVPUB_ROW_ARGS
 }
@@ -690,13 +735,19 @@ hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t
         const uint16_t* ix = p.indexer + t * p.indexer_stride;
         const int64_t* sl = p.slots + t;
         const int64_t written = n * (int64_t)num_replicas * kCacheBytesPerToken;
+        // every layer spans less than 4 GiB: 32-bit offsets (the write-through
+        // path's buffer stores need them)
         const bool offsets32 = p.main_region != 0 && p.idx_region != 0;
-        if (written <= kStreamingStoreBytes)
-            launch_r<true, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
-        else if (written > kWriteThroughBytes && offsets32)
-            launch_r<false, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
-        else
-            launch_r<false, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, (uint32_t)n, p);
+        const uint32_t un = (uint32_t)n;
+        if (written <= kStreamingStoreBytes) {
+            if (offsets32) launch_r<true, false, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+            else launch_r<true, false, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+        } else if (written > kWriteThroughBytes && offsets32) {
+            launch_r<false, true, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+        } else {
+            if (offsets32) launch_r<false, false, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+            else launch_r<false, false, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
