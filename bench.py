@@ -3,15 +3,20 @@
 
 A step is one replay of the captured graph of the model shape: 61 sparse
 layers, each a kvpub_store of T=4096 tokens into R=2 replica caches of 8192
-64-slot pages followed by one kvpub_fence (so every part of the hot path runs:
-slot decode, row loads, tile amax, scale, e4m3 quantization, row packing, the
-R-way fan-out stores, the fence, graph replay).  Inputs are seeded N(0,1) bf16
-rows already resident in HBM; the cache layout is the one the library
-documents (656-byte Main-KV rows, 8448-byte Indexer-K pages).
+64-slot pages followed by one kvpub_fence (system-scope release, then acquire
+wait on the epoch), so every part of the hot path runs: slot decode, row
+loads, tile amax, scale, e4m3 quantization, row packing, the R-way fan-out
+stores, the fence, graph replay.  Inputs are seeded N(0,1) bf16 rows already
+resident in HBM; the cache layout is the one the library documents (656-byte
+Main-KV rows, 8448-byte Indexer-K pages).  After the timed replays the
+replicas are checked for identity and one layer against the CPU oracle.
 
 Printed: one JSON line with tokens/s (value), the store kernel's achieved HBM
-bandwidth against the 8 TB/s peak (roofline), the fence cost per layer, and
-the CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
+bandwidth against the 8 TB/s peak (roofline), the fence cost per layer in its
+three forms (release + acquire wait, release only, and the pages' earlier
+two-launch fence with a host-held epoch), the plain-stream floor for the same
+bytes, the prefill and heavy-tail store shapes, and the CPU oracle timed on a
+bounded sample of the same workload (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -59,8 +64,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill / heavy-tail store-only figures")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--cpu-runs", type=int, default=5,
+                    help="runs per CPU-baseline leg (the median is reported)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (torch copy_) three times, so that "
                          "memory-traffic counters can be scaled by a kernel of known size")
@@ -113,8 +118,7 @@ def main():
     L, T = W.GRAPH_LAYERS, W.GRAPH_T
     layout = W.graph_layout()
     R = layout.replicas
-    print(f"[bench] {dev_name}: graph workload {L} layers x T={T}, R={R}, pages={layout.num_pages}",
-          file=sys.stderr, flush=True)
+    log(f"{dev_name}: graph workload {L} layers x T={T}, R={R}, pages={layout.num_pages}")
 
     main_bufs = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
     idx_bufs = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
@@ -122,9 +126,18 @@ def main():
         layout.fill_device(b, "main")
     for b in idx_bufs:
         layout.fill_device(b, "idx")
-    cfg = kvpub.kvpub_config_init(R, L, layout.num_pages)
-    st, ctx = kvpub.kvpub_create(cfg, [b.data_ptr() for b in main_bufs], [b.data_ptr() for b in idx_bufs])
-    kvpub.check(st, "kvpub_create")
+    mbp, ibp = [b.data_ptr() for b in main_bufs], [b.data_ptr() for b in idx_bufs]
+
+    def context(flags=0):
+        cfg = kvpub.kvpub_config_init(R, L, layout.num_pages)
+        cfg.flags = flags
+        st, c = kvpub.kvpub_create(cfg, mbp, ibp)
+        kvpub.check(st, "kvpub_create")
+        return c
+
+    ctx = context()                                           # release + acquire-wait fence (default)
+    ctx_rel = context(kvpub.KVPUB_CONFIG_FENCE_RELEASE_ONLY)  # release-only fence
+    ctx_two = context()                                       # the two-launch host-epoch fence
 
     lat = torch.empty((L, T, 512), dtype=torch.bfloat16, device="cuda")
     rope = torch.empty((L, T, 64), dtype=torch.bfloat16, device="cuda")
@@ -142,11 +155,15 @@ def main():
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
 
+    def store(c, l):
+        kvpub.check(kvpub.kvpub_store(c, l, T, lat[l].data_ptr(), 512, rope[l].data_ptr(), 64,
+                                      idx[l].data_ptr(), 128, slots.data_ptr(), sh))
+
     # --- the timed steps: K replays of the full store + fence graph -------------
     for _ in range(args.warmup):
         kvpub.check(kvpub.kvpub_graph_replay(graph, sh))
     torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    log(f"warmup {args.warmup} done; timing {args.steps} steps")
     with Timer(torch, stream) as tm:
         for _ in range(args.steps):
             kvpub.kvpub_graph_replay(graph, sh)
@@ -154,64 +171,87 @@ def main():
     st, epoch = kvpub.kvpub_epoch_read(ctx, 0)
     kvpub.check(st)
     assert epoch == L * (args.warmup + args.steps), epoch
-    tokens_per_s = valid * L / (step_ms * 1e-3)
-
-    # --- store kernel alone: the same 61 stores captured without fences ---------
-    g_store = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g_store, stream=stream):
-            for l in range(L):
-                kvpub.check(kvpub.kvpub_store(ctx, l, T, lat[l].data_ptr(), 512, rope[l].data_ptr(), 64,
-                                              idx[l].data_ptr(), 128, slots.data_ptr(), sh))
-    reps = max(4, args.steps // 4)
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            g_store.replay()
-        with Timer(torch, stream) as ts:
-            for _ in range(reps):
-                g_store.replay()
-    store_us = ts.ms * 1e3 / (reps * L)
-    store_bytes = alg_bytes(valid, R)
-    store_gbps = store_bytes / (store_us * 1e-6) / 1e9
-
-    # --- fence alone: 61 fences captured back to back --------------------------
-    g_fence = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g_fence, stream=stream):
-            for l in range(L):
-                kvpub.check(kvpub.kvpub_fence(ctx, 0, sh))
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            g_fence.replay()
-        with Timer(torch, stream) as tf:
-            for _ in range(reps):
-                g_fence.replay()
-    fence_us_alone = tf.ms * 1e3 / (reps * L)
-    fence_us_in_step = (step_ms * 1e3 - store_us * L) / L
-
-    # --- the pages' one-launch vs two-launch fence, by launch count only: the
-    # same layers with two fence launches each (a stand-in for a signal launch
-    # followed by a wait launch; the host-held-epoch design itself is not built)
-    g_two = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g_two, stream=stream):
-            for l in range(L):
-                kvpub.check(kvpub.kvpub_store(ctx, l, T, lat[l].data_ptr(), 512, rope[l].data_ptr(), 64,
-                                              idx[l].data_ptr(), 128, slots.data_ptr(), sh))
-                kvpub.check(kvpub.kvpub_fence(ctx, 0, sh))
-                kvpub.check(kvpub.kvpub_fence(ctx, 0, sh))
-    with torch.cuda.stream(stream):
-        for _ in range(2):
-            g_two.replay()
-        with Timer(torch, stream) as t2:
-            for _ in range(reps):
-                g_two.replay()
-    two_launch_layer_us = t2.ms * 1e3 / (reps * L)
     st, invalid, flags = kvpub.kvpub_error_read(ctx, False)
     kvpub.check(st)
     assert invalid == 0 and flags == 0
+    tokens_per_s = valid * L / (step_ms * 1e-3)
+    log("verifying the timed steps' output")
+    check = verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer=L // 2)
+
+    def graph_us(body, reps):
+        """Average microseconds per replay of a torch graph of body()."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                body()
+            for _ in range(2):
+                g.replay()
+            with Timer(torch, stream) as t:
+                for _ in range(reps):
+                    g.replay()
+        return t.ms * 1e3 / reps, g
+
+    reps = max(4, args.steps // 4)
+
+    # --- store kernel alone: the same 61 stores captured without fences ---------
+    us, _ = graph_us(lambda: [store(ctx, l) for l in range(L)], reps)
+    store_us = us / L
+    store_bytes = alg_bytes(valid, R)
+    store_gbps = store_bytes / (store_us * 1e-6) / 1e9
+
+    # --- the fence in its three forms ------------------------------------------
+    fence_alone = {}
+    fence_alone["acquire"], _ = graph_us(lambda: [kvpub.check(kvpub.kvpub_fence(ctx, 0, sh)) for _ in range(L)], reps)
+    fence_alone["release"], _ = graph_us(
+        lambda: [kvpub.check(kvpub.kvpub_fence(ctx_rel, 0, sh)) for _ in range(L)], reps)
+    fence_alone["two_launch"], _ = graph_us(
+        lambda: [kvpub.check(kvpub.kvpub_fence_host_epoch(ctx_two, 0, sh)) for _ in range(L)], reps)
+    st, rel_graph = kvpub.kvpub_graph_create(ctx_rel, ios, 0)
+    kvpub.check(st, "kvpub_graph_create (release only)")
+    for _ in range(2):
+        kvpub.check(kvpub.kvpub_graph_replay(rel_graph, sh))
+    with Timer(torch, stream) as trel:
+        for _ in range(args.steps):
+            kvpub.kvpub_graph_replay(rel_graph, sh)
+    rel_step_ms = trel.ms / args.steps
+    kvpub.kvpub_graph_destroy(rel_graph)
+    st, e_two0 = kvpub.kvpub_epoch_read(ctx_two, 0)
+    kvpub.check(st)
+    two_reps = reps
+    two_us, _ = graph_us(lambda: [(store(ctx_two, l), kvpub.check(kvpub.kvpub_fence_host_epoch(ctx_two, 0, sh)))
+                                  for l in range(L)], two_reps)
+    st, e_two = kvpub.kvpub_epoch_read(ctx_two, 0)
+    kvpub.check(st)
+    for c in (ctx, ctx_rel, ctx_two):
+        st, invalid, flags = kvpub.kvpub_error_read(c, False)
+        kvpub.check(st)
+        assert invalid == 0 and flags == 0
+    per_layer = lambda ms: ms * 1e3 / L
+    fence = {
+        "form": "system-scope release RMW of the lane's epoch, then acquire loads of it (the default)",
+        "in_step": round(per_layer(step_ms) - store_us, 3),
+        "alone": round(fence_alone["acquire"] / L, 3),
+        "layer_us": round(per_layer(step_ms), 3),
+        "release_only": {"in_step": round(per_layer(rel_step_ms) - store_us, 3),
+                         "alone": round(fence_alone["release"] / L, 3),
+                         "layer_us": round(per_layer(rel_step_ms), 3),
+                         "ms_per_step": round(rel_step_ms, 4)},
+        "two_launch_host_epoch": {
+            "in_step": round(two_us / L - store_us, 3),
+            "alone": round(fence_alone["two_launch"] / L, 3),
+            "layer_us": round(two_us / L, 3),
+            "epoch_before_capture": e_two0,
+            "epoch_after_replays": e_two,
+            "replays": two_reps + 2,
+            "epoch_if_replays_advanced_it": e_two0 + L * (two_reps + 2)},
+        "how": "in_step = step time / 61 - store time per launch; alone = a graph of 61 fences / 61; "
+               "two_launch_host_epoch = a publish kernel and a wait kernel per fence with the epoch counted on "
+               "the host (the design the single-launch fence replaces), same 61-layer graph; its epoch stays "
+               "at the value published at capture however often the graph is replayed",
+    }
 
     gather = None if args.no_extras else gather_line(torch, kvpub, ctx, slots, T, valid, stream)
+    floor_graph = None if args.no_extras else floor_graph_layer(torch, stream, L, valid, R, store_us)
 
     extras = {}
     decode = fanout = None
@@ -243,7 +283,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "store_kernel<2, true, false>",
+            "kernel": "store_kernel<2, true, false, true>",
             "achieved": round(store_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -254,17 +294,12 @@ def main():
             "avg_launch_us": round(store_us, 3),
             "how": "HIP events around replays of a graph of the 61 store launches alone",
         },
-        "fence_us_per_layer": {
-            "in_step": round(fence_us_in_step, 3),
-            "alone": round(fence_us_alone, 3),
-            "how": "in_step = (step time - 61 x store time) / 61; alone = graph of 61 fences / 61",
-            "layer_us_one_fence_launch": round(step_ms * 1e3 / L, 3),
-            "layer_us_two_fence_launches": round(two_launch_layer_us, 3),
-            "two_launch_how": "the same 61-layer graph with two fence launches per layer, a stand-in for the "
-                              "pages' signal-then-wait fence (launch count only)",
-        },
+        "fence_us_per_layer": fence,
         "store_us_per_layer": round(store_us, 3),
+        "verified": check,
     }
+    if floor_graph:
+        result["roofline"]["floor"] = floor_graph
     if extras:
         result["store_only"] = extras
     if decode:
@@ -277,23 +312,122 @@ def main():
     kvpub.kvpub_graph_destroy(graph)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(lat, rope, idx, slots_np, layout, args.cpu_seconds)
+        def gpu_layer(l):
+            """Replica 0's and replica R-1's bytes of layer l (Main-KV, Indexer-K) on the host."""
+            ms, is_ = layout.main_layer_stride, layout.idx_layer_stride
+            return [(b[l * ms:(l + 1) * ms].cpu().numpy(), c[l * is_:(l + 1) * is_].cpu().numpy())
+                    for b, c in ((main_bufs[0], idx_bufs[0]), (main_bufs[-1], idx_bufs[-1]))]
+        result["cpu_baseline"] = cpu_baseline(lat, rope, idx, slots_np, layout, args.cpu_runs, gpu_layer)
 
-    kvpub.check(kvpub.kvpub_destroy(ctx))
+    for c in (ctx, ctx_rel, ctx_two):
+        kvpub.check(kvpub.kvpub_destroy(c))
     print(json.dumps(result), flush=True)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def written_offsets(torch, layout, layer, slots_np):
+    """Device byte offsets of the rows a store of `slots_np` writes in `layer`:
+    (Main-KV [n, 656], Indexer-K codes [n, 128], Indexer-K scale [n, 4], valid mask)."""
+    valid = (slots_np >= 0) & (slots_np < layout.capacity)
+    s = torch.from_numpy(slots_np[valid]).to("cuda")
+    p, o = s // 64, s % 64
+    ar = lambda n: torch.arange(n, device="cuda", dtype=torch.int64)[None, :]
+    mb = layer * layout.main_layer_stride + p * layout.main_page_stride + o * 656
+    ib = layer * layout.idx_layer_stride + p * layout.idx_page_stride
+    return mb[:, None] + ar(656), (ib + o * 128)[:, None] + ar(128), (ib + 8192 + o * 4)[:, None] + ar(4), valid
+
+
+def verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer):
+    """After the timed replays: every replica equals replica 0 (whole buffers); in
+    `layer`, every byte outside the written rows still holds the fill pattern; the
+    end canaries are intact.  (The written bytes are compared with the CPU oracle in
+    the cpu_baseline leg, which runs the oracle on the same inputs.)"""
+    from replicated_fp8_sparse_amd.workloads import FILL, GUARD, CANARY_BYTES
+    torch.cuda.synchronize()
+    for r in range(1, len(main_bufs)):
+        assert torch.equal(main_bufs[r], main_bufs[0]), f"Main-KV replica {r} differs from replica 0"
+        assert torch.equal(idx_bufs[r], idx_bufs[0]), f"Indexer-K replica {r} differs from replica 0"
+    mo, co, so, valid = written_offsets(torch, layout, layer, slots_np)
+    for buf, offs, lstride in ((main_bufs[0], (mo,), layout.main_layer_stride),
+                               (idx_bufs[0], (co, so), layout.idx_layer_stride)):
+        keep = torch.ones(lstride, dtype=torch.bool, device="cuda")
+        for off in offs:
+            keep[(off - layer * lstride).reshape(-1)] = False
+        seg = buf[layer * lstride:(layer + 1) * lstride]
+        assert bool((seg[keep] == FILL).all()), f"layer {layer}: a byte outside the written rows changed"
+    for buf in main_bufs + idx_bufs:
+        assert bool((buf[-CANARY_BYTES:] == GUARD).all()), "end-of-buffer canary changed"
+    return {"replicas_identical": True, "untouched_bytes_layer": layer, "rows_written_per_layer": int(valid.sum()),
+            "how": "after the timed replays: torch.equal of every replica with replica 0, every byte outside one "
+                   "layer's written rows against the fill pattern, the end canaries; the CPU oracle's bytes for "
+                   "the last layer are compared in cpu_baseline (oracle_layer_check)"}
+
+
+def floor_us(torch, stream, fl, inp, in_bytes, outs, out_bytes, n, policy, reps=8):
+    """Average microseconds of floor launches over n rotated input / output regions
+    (a torch graph of the n launches, replayed)."""
+    sh = stream.cuda_stream
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                rc = fl.kvpub_floor_stream(inp.data_ptr() + i * in_bytes, in_bytes,
+                                           [o.data_ptr() + i * out_bytes for o in outs], out_bytes, policy, sh)
+                assert rc == 0, rc
+        g.replay()
+        with Timer(torch, stream) as t:
+            for _ in range(reps):
+                g.replay()
+    del g
+    return t.ms * 1e3 / (reps * n)
+
+
+def floor_line(torch, stream, valid, R, n, store_us):
+    """The plain-stream floor for the bytes of a store launch: read valid x 1408 B,
+    write valid x 788 B to each of R outputs, n launches over distinct regions."""
+    from replicated_fp8_sparse_amd import floor as fl
+    in_bytes = valid * READ_BYTES_PER_TOKEN
+    out_bytes = valid * WRITE_BYTES_PER_TOKEN_PER_REPLICA
+    in_bytes, out_bytes = in_bytes - in_bytes % 16, out_bytes - out_bytes % 16
+    inp = torch.empty(n * in_bytes, dtype=torch.uint8, device="cuda")
+    inp.fill_(7)
+    outs = [torch.empty(n * out_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    res = {name: round(floor_us(torch, stream, fl, inp, in_bytes, outs, out_bytes, n, pol), 3)
+           for name, pol in fl.POLICIES.items()}
+    best = min(res.values())
+    del inp, outs
+    torch.cuda.empty_cache()
+    return {"floor_us": best, "by_policy_us": res, "store_frac_of_floor": round(best / store_us, 4),
+            "how": f"a trivial kernel reading {in_bytes} B and writing {out_bytes} B to each of {R} buffers as "
+                   f"whole 16-B pieces, {n} launches over distinct regions in a replayed graph; the fastest store "
+                   "policy"}
+
+
+def floor_graph_layer(torch, stream, L, valid, R, store_us):
+    log("floor for the graph layer")
+    return floor_line(torch, stream, valid, R, L, store_us)
 
 
 def store_only_extras(torch, kvpub, W, stream):
     """Store-kernel bandwidth on the prefill (T=8192, R=4) and heavy-tail (T=32768, R=4)
-    workloads: eager back-to-back launches over rotated input copies, HIP events.  The
-    heavy shape is run twice: on ordinary device allocations and on VMM-backed replicas
-    (kvpub_vmm_create), whose mappings the kernel reaches through the same pointers."""
+    workloads.  Warm: a replayed graph of launches over rotated input copies and slot
+    mappings that write disjoint page sets (16 prefill mappings in windows of 1024 pages,
+    8 heavy mappings over successive 512-page blocks of one page permutation), so the
+    bytes a replay touches (0.6 resp. 1.2 GB) exceed the 256 MB memory-side cache and the
+    figure is one of HBM.  Cold: single launches, each after a 1 GiB read that leaves no
+    dirty line behind.  The heavy shape runs again on VMM-backed replicas."""
+    from replicated_fp8_sparse_amd import floor as _fl  # noqa: F401  (fails loudly if unbuilt)
     out = {}
     sh = stream.cuda_stream
-    for name, fn, copies, vmm in (("prefill_T8192_R4", W.prefill, 8, False), ("heavy_T32768_R4", W.heavy, 8, False),
-                                  ("heavy_T32768_R4_vmm", W.heavy, 8, True)):
+    for name, fn, vmm in (("prefill_T8192_R4", W.prefill, False), ("heavy_T32768_R4", W.heavy, False),
+                          ("heavy_T32768_R4_vmm", W.heavy, True)):
         layout, x = fn()
-        print(f"[bench] store-only {name}", file=sys.stderr, flush=True)
+        rot = W.prefill_rotation_slots(16) if fn is W.prefill else W.heavy_rotation_slots(8)
+        copies = len(rot)
+        log(f"store-only {name}")
         R = layout.replicas
         cfg = kvpub.kvpub_config_init(R, 1, layout.num_pages)
         storage = None
@@ -316,32 +450,47 @@ def store_only_extras(torch, kvpub, W, stream):
         lat = torch.from_numpy(x.latent.view(np.int16)).to("cuda").repeat(copies, 1, 1)
         rope = torch.from_numpy(x.rope.view(np.int16)).to("cuda").repeat(copies, 1, 1)
         idx = torch.from_numpy(x.indexer.view(np.int16)).to("cuda").repeat(copies, 1, 1)
-        slots = torch.from_numpy(x.slots).to("cuda")
+        slots = torch.from_numpy(np.stack(rot)).to("cuda")
+        same = torch.from_numpy(x.slots).to("cuda")
         valid = int(((x.slots >= 0) & (x.slots < layout.capacity)).sum())
+        assert all(int(((s >= 0) & (s < layout.capacity)).sum()) == valid for s in rot)
 
-        def launch(c):
+        def launch(c, slot_ptr=None):
             return kvpub.kvpub_store(ctx, 0, T, lat[c].data_ptr(), 512, rope[c].data_ptr(), 64,
-                                     idx[c].data_ptr(), 128, slots.data_ptr(), sh)
+                                     idx[c].data_ptr(), 128, slots[c].data_ptr() if slot_ptr is None else slot_ptr, sh)
 
-        for c in range(copies):
-            kvpub.check(launch(c))
-        n = 8 * copies
-        with Timer(torch, stream) as tm:
-            for i in range(n):
-                launch(i % copies)
-        us = tm.ms * 1e3 / n
+        def warm(body):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    for c in range(copies):
+                        kvpub.check(body(c))
+                g.replay()
+                reps = 8
+                with Timer(torch, stream) as tm:
+                    for _ in range(reps):
+                        g.replay()
+            del g
+            return tm.ms * 1e3 / (reps * copies)
+
+        us = warm(launch)
+        us_same = warm(lambda c: launch(c, same.data_ptr()))
         cold = cold_launch_us(torch, stream, launch, copies)
         b = alg_bytes(valid, R)
+        gb = lambda t: b / (t * 1e-6) / 1e9
         out[name] = {"avg_launch_us": round(us, 3), "alg_bytes": b,
-                     "gbps": round(b / (us * 1e-6) / 1e9, 1),
-                     "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "gbps": round(gb(us), 1), "frac": round(gb(us) / HBM_PEAK_GBPS, 4),
                      "tokens_per_s": round(valid / (us * 1e-6), 1),
-                     "cold_launch_us": round(cold, 3),
-                     "cold_frac": round(b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "cold_launch_us": round(cold, 3), "cold_frac": round(gb(cold) / HBM_PEAK_GBPS, 4),
+                     "same_slots_launch_us": round(us_same, 3),
                      "storage": "vmm" if vmm else "device allocations",
-                     "how": "warm: back-to-back launches over rotated input copies; cold: each launch "
-                            "timed alone after writing a 1 GiB scratch buffer (flushes L2 and the "
-                            "256 MB memory-side cache)"}
+                     "how": f"warm: a replayed graph of {copies} launches over rotated input copies and slot "
+                            "mappings writing disjoint page sets (bytes touched per replay exceed the 256 MB "
+                            "memory-side cache); cold: median of single launches, each after reading a 1 GiB "
+                            "buffer (no dirty lines left); same_slots: the warm graph with one slot mapping "
+                            "(rewrites the same pages every launch)"}
+        if not vmm:
+            out[name]["floor"] = floor_line(torch, stream, valid, R, copies, us)
         kvpub.check(kvpub.kvpub_destroy(ctx))
         if storage is not None:
             kvpub.check(kvpub.kvpub_vmm_destroy(storage), "kvpub_vmm_destroy")
@@ -421,7 +570,7 @@ def gather_line(torch, kvpub, ctx, slots, T, valid, stream):
     """The reader side on the graph workload's layer: kvpub_gather of the T=4096
     slots from replica 0 back to bf16 rows, over the 61 layers.  Timed as replays of
     a graph of the 61 gathers (as the store is), eagerly back to back (host launch
-    cost included), and cold (one launch after a 1 GiB scratch write)."""
+    cost included), and cold (one launch after a 1 GiB read)."""
     sh = stream.cuda_stream
     L = 61
     lat = torch.empty((T, 512), dtype=torch.bfloat16, device="cuda")
@@ -459,16 +608,17 @@ def gather_line(torch, kvpub, ctx, slots, T, valid, stream):
             "cold_launch_us": round(cold, 3),
             "how": "replays of a graph of 61 gathers over the 61 layer caches of replica 0 (avg), the same "
                    "launches eagerly back to back (eager, host launch cost included), and single launches "
-                   "after a 1 GiB scratch write (cold); bytes = 788 B read + 1408 B written per token"}
+                   "after a 1 GiB read (cold); bytes = 788 B read + 1408 B written per token"}
 
 
 def cold_launch_us(torch, stream, launch, copies, n=12):
-    """Median duration of single store launches, each after a 1 GiB scratch write."""
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    """Median duration of single launches, each after reading a 1 GiB buffer (which
+    evicts the L2s and the memory-side cache and leaves no dirty line behind)."""
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
     times = []
     with torch.cuda.stream(stream):
         for i in range(n):
-            scratch.fill_(i & 0xFF)
+            sink = scratch.sum(dtype=torch.int64)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -476,6 +626,7 @@ def cold_launch_us(torch, stream, launch, copies, n=12):
             b.record(stream)
             b.synchronize()
             times.append(a.elapsed_time(b) * 1e3)
+    assert int(sink) == 1 << 28
     del scratch
     torch.cuda.empty_cache()
     return float(np.median(times))
@@ -536,13 +687,13 @@ def decode_eager(torch, kvpub, W, stream):
                    "(host launch cost included), and the same sequence captured once and replayed"}
 
 
-def cpu_baseline(lat, rope, idx, slots_np, layout, seconds):
+def cpu_baseline(lat, rope, idx, slots_np, layout, runs, gpu_layer=None):
     """The CPU oracle (plain C, as it stands) on a bounded sample of the same workload:
-    the graph workload's layers one after another, into host replicas of one
-    layer-cache, until about `seconds` of wall time per leg.  Timed single-threaded
-    and with one thread per host core (at most 16) over contiguous token ranges of
-    each layer (race-free: the valid slots of a layer are distinct; the C calls
-    release the interpreter lock)."""
+    graph-workload layers one after another into host replicas of one layer-cache.
+    Two legs, each run `runs` times (the median is reported, with the spread):
+    single-threaded over 8 layers per run, and with one thread per host core (at most
+    16) over contiguous token ranges of each of the 61 layers per run (race-free: a
+    layer's valid slots are distinct; the C calls release the interpreter lock)."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle
     orc = oracle.get()
@@ -552,6 +703,8 @@ def cpu_baseline(lat, rope, idx, slots_np, layout, seconds):
     idxs = [i0.copy() for _ in range(layout.replicas)]
     valid_per_layer = int(((slots_np >= 0) & (slots_np < layout.capacity)).sum())
     T = slots_np.size
+    u16 = lambda t: t.cpu().view(torch_int16()).numpy().view(np.uint16)
+    host = [(u16(lat[l]), u16(rope[l]), u16(idx[l])) for l in range(L)]
 
     def store_range(x_l, x_r, x_i, a, b):
         orc.store(mains, idxs, num_pages=layout.num_pages,
@@ -559,39 +712,49 @@ def cpu_baseline(lat, rope, idx, slots_np, layout, seconds):
                   idx_page_stride=layout.idx_page_stride, idx_layer_stride=layout.idx_layer_stride,
                   layer=0, latent=x_l[a:b], rope=x_r[a:b], indexer=x_i[a:b], slot_mapping=slots_np[a:b])
 
-    def leg(threads, budget):
-        done, elapsed, layers = 0, 0.0, 0
+    def run(threads, layers, ex):
         bounds = np.linspace(0, T, threads + 1).astype(int)
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            for l in range(L):
-                x_l = lat[l].cpu().view(torch_int16()).numpy().view(np.uint16)
-                x_r = rope[l].cpu().view(torch_int16()).numpy().view(np.uint16)
-                x_i = idx[l].cpu().view(torch_int16()).numpy().view(np.uint16)
-                t0 = time.perf_counter()
-                if threads == 1:
-                    store_range(x_l, x_r, x_i, 0, T)
-                else:
-                    list(ex.map(lambda ab: store_range(x_l, x_r, x_i, ab[0], ab[1]),
-                                zip(bounds[:-1], bounds[1:])))
-                elapsed += time.perf_counter() - t0
-                done += valid_per_layer
-                layers += 1
-                if elapsed >= budget:
-                    break
-        return done / elapsed, layers, elapsed
+        t0 = time.perf_counter()
+        for l in range(layers):
+            x_l, x_r, x_i = host[l]
+            if threads == 1:
+                store_range(x_l, x_r, x_i, 0, T)
+            else:
+                list(ex.map(lambda ab: store_range(x_l, x_r, x_i, ab[0], ab[1]), zip(bounds[:-1], bounds[1:])))
+        return valid_per_layer * layers / (time.perf_counter() - t0)
 
-    one, l1, e1 = leg(1, seconds / 2)
+    def leg(threads, layers):
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            rates = [run(threads, layers, ex) for _ in range(runs)]
+        return float(np.median(rates)), min(rates), max(rates)
+
+    one_layers, many_layers = 8, L
+    one = leg(1, one_layers)
     cores = max(1, min(os.cpu_count() or 1, 16))
-    many, lm, em = leg(cores, seconds / 2) if cores > 1 else (one, l1, e1)
-    return {"value": round(many, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"graph workload layers (T=4096, R=2, 8192 pages) through the C oracle: "
-                      f"{lm} layers on {cores} threads in {em:.1f} s; single-threaded "
-                      f"{l1} layers in {e1:.1f} s",
-            "single_thread_value": round(one, 1),
-            "gbps": round(alg_bytes(many, layout.replicas) / 1e9, 3),
-            "single_thread_gbps": round(alg_bytes(one, layout.replicas) / 1e9, 3),
+    many = leg(cores, many_layers)
+    # Every run ends with the last layer, and every layer uses the same slots, so the
+    # host layer-cache now holds the oracle's encoding of the last layer's inputs:
+    # compare it, written rows and untouched bytes alike, with that layer on the GPU.
+    check = None
+    if gpu_layer is not None:
+        for r, (gm, gi) in enumerate(gpu_layer(L - 1)):
+            assert np.array_equal(gm, mains[0][:gm.size]), f"GPU Main-KV layer {L - 1} differs from the oracle"
+            assert np.array_equal(gi, idxs[0][:gi.size]), f"GPU Indexer-K layer {L - 1} differs from the oracle"
+        check = {"layer": L - 1, "bytes_compared": int(2 * (gm.size + gi.size)), "equal": True,
+                 "how": "the oracle's host layer-cache after the timed runs (the last layer's rows) against "
+                        "that layer of the first and last GPU replicas, every byte"}
+    return {"value": round(many[0], 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"graph workload layers (T=4096, R=2, 8192 pages) through the C oracle: {runs} runs of "
+                      f"{many_layers} layers on {cores} threads (median reported) and {runs} runs of "
+                      f"{one_layers} layers single-threaded",
+            "runs": runs, "min": round(many[1], 1), "max": round(many[2], 1),
+            "single_thread_value": round(one[0], 1),
+            "single_thread_min": round(one[1], 1), "single_thread_max": round(one[2], 1),
+            "gbps": round(alg_bytes(many[0], layout.replicas) / 1e9, 3),
+            "single_thread_gbps": round(alg_bytes(one[0], layout.replicas) / 1e9, 3),
             "host_cpus": os.cpu_count(),
-            "cpu_model": host_cpu_model()}
+            "cpu_model": host_cpu_model(),
+            "oracle_layer_check": check}
 
 
 def host_cpu_model():

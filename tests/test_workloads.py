@@ -137,3 +137,29 @@ def test_layout_fill_and_guards():
     assert np.all(m[-W.CANARY_BYTES:] == W.GUARD)
     ipages = i[:-W.CANARY_BYTES].reshape(6, 64 * 132 + 64)
     assert np.all(ipages[:, :64 * 132] == W.FILL) and np.all(ipages[:, 64 * 132:] == W.GUARD)
+
+
+def test_rotation_slots_write_disjoint_pages():
+    """The benchmark's warm prefill and heavy-tail figures rotate over slot mappings that
+    write disjoint page sets; each mapping keeps its workload's recipe."""
+    from replicated_fp8_sparse_amd import workloads as W
+    _, hx = W.heavy()
+    heavy = W.heavy_rotation_slots(8)
+    assert np.array_equal(heavy[0], hx.slots)                       # the heavy workload's own mapping first
+    prefill = W.prefill_rotation_slots(16)
+    for maps, pages_per_map in ((heavy, 512), (prefill, None)):
+        seen = set()
+        for s in maps:
+            valid = s[s >= 0]
+            assert np.unique(valid).size == valid.size              # distinct slots
+            pages = set((valid // 64).tolist())
+            assert not (pages & seen), "two mappings share a page"
+            seen |= pages
+            if pages_per_map:
+                assert len(pages) == pages_per_map and np.array_equal(valid % 64, np.arange(valid.size) % 64)
+    for j, s in enumerate(prefill):
+        assert s.size == 8192 and np.all(s[8155:] == -1) and np.all(s[:8155] >= 0)
+        assert np.all(s[:8155] // 64 // 1024 == j)                  # inside the mapping's own window
+        runs = np.split(s[:8155], np.nonzero(np.diff(s[:8155]) != 1)[0] + 1)
+        assert all(r[0] % 64 == 0 for r in runs)                    # runs start at page boundaries
+        assert sum(r.size for r in runs) == 8155
