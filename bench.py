@@ -41,15 +41,20 @@ KERNEL_SOURCE = os.path.join(ROOT, "replicated_fp8_sparse_amd", "csrc", "store_k
 
 
 def measured_traffic():
-    """HBM bytes per store launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    record (scaled by a 256 MiB copy), or None if the kernel source changed since."""
+    """(HBM bytes per store launch, how) from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, or (None, why) if the kernel source changed since."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_RECORD))
         src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except (OSError, ValueError):
-        return None
-    return rec["traffic_bytes_per_launch"] if rec.get("source_sha256") == src else None
+        return None, "no traffic record"
+    if rec.get("source_sha256") != src:
+        return None, "the kernel source changed since the counters were taken"
+    cal = rec["calibration"]
+    return rec["traffic_bytes_per_launch"], (
+        f"bytes per launch: rocprofv3 FETCH_SIZE x{cal['fetch_factor']} + WRITE_SIZE x{cal['write_factor']}, "
+        "the factors from the floor kernel moving the same bytes (profiles/store_kernel_graph_T4096_R2_traffic.json)")
 
 
 def alg_bytes(valid_tokens, replicas):
@@ -260,6 +265,7 @@ def main():
         decode = decode_eager(torch, kvpub, W, stream)
         fanout = fanout_ab(torch, kvpub, W, stream)
 
+    traffic, traffic_how = measured_traffic()
     result = {
         "metric": "cache-store tokens/sec and achieved HBM GB/s (% of peak); fence µs/layer",
         "value": round(tokens_per_s, 1),
@@ -288,8 +294,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(store_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(),
-            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0, scaled by a 256 MiB copy)",
+            "traffic": traffic,
+            "traffic_unit": traffic_how,
             "alg_bytes_per_launch": store_bytes,
             "avg_launch_us": round(store_us, 3),
             "how": "HIP events around replays of a graph of the 61 store launches alone",
