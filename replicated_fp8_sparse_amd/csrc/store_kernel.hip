@@ -73,12 +73,15 @@ constexpr int64_t kSmallBatchTokens = 1024;
 //     L2 for the end-of-kernel write-back, which a latency-bound launch would
 //     otherwise wait for, while the partial lines still merge in L2.
 //   WT (a launch writing more than kWriteThroughBytes, more than the eight
-//     4 MB L2s can hold): every piece is a buffer store with the device-
-//     coherence bit, written through this XCD's L2 instead of held dirty in
-//     it, so the writes stream out while the kernel runs instead of being
-//     evicted later.  Buffer offsets are 32-bit, so WT needs each replica's
-//     layer to span less than 2^32 bytes; the buffer's range check
-//     (num_records = the layer's span) drops any store outside the layer.
+//     4 MB L2s can hold): the whole-line pieces are buffer stores with the
+//     device-coherence bit, written through this XCD's L2 instead of held
+//     dirty in it, so the writes stream out while the kernel runs instead of
+//     being evicted later; the partial pieces (the 16-byte Indexer-K scale
+//     runs, four waves to a 64-byte line) stay write-back, so they merge in
+//     L2 instead of reaching memory as partial writes.  Buffer offsets are
+//     32-bit, so WT needs each replica's layer to span less than 2^32 bytes;
+//     the buffer's range check (num_records = the layer's span) drops any
+//     whole-line store outside the layer.
 //   otherwise (launches in between, or layers too large for WT): ordinary
 //     write-back stores, which the L2s absorb.
 template <bool NT, class T>
@@ -95,7 +98,7 @@ constexpr int kDeviceCoherent = 16;      // buffer cache-policy bits: sc1
 // which the store instruction takes as is (no 64-bit address arithmetic).
 template <bool NT, bool WT, bool whole, class T, class O>
 __device__ __forceinline__ void put_at(gbyte* base, uint32_t region, O off, T v) {
-    if constexpr (WT) {
+    if constexpr (WT && whole) {
         const __amdgpu_buffer_rsrc_t r =
             __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)region, kRsrcWord3);
         const int o = (int)(uint32_t)off;
