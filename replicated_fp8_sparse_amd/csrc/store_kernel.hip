@@ -61,6 +61,7 @@ constexpr uint32_t kRunBytes = 4 * 656;   // 2624 = 164 x 16 B
 constexpr int64_t kCacheBytesPerToken = 656 + 128 + 4;              // per replica
 constexpr int64_t kStreamingStoreBytes = int64_t(16) << 20;         // launches writing at most this stream
 constexpr int64_t kWriteThroughBytes = int64_t(32) << 20;           // more than the 8 L2s hold: write through
+constexpr int kBlockRunWaves = 8;   // waves per block of those launches (block runs of 32 rows, 20,992 bytes)
 // Batches up to this many tokens take small_store_kernel (up to twice as many
 // with one or two replicas): measured crossover against the main kernel.
 constexpr int64_t kSmallBatchTokens = 1024;
@@ -403,9 +404,12 @@ __device__ __forceinline__ Dest<O32> destinations(int64_t s0, int64_t s1, int64_
 //   Indexer-K scale   -> page bytes [8192 + 4*(slot%64), +4) (lane 16g)
 // The five rounds are computed as one straight-line block (their reductions
 // and scale sequences interleave); only the stores are conditional.
-template <int R, bool NT, bool WT, bool O32>
+// WPB (waves per block) above 4 turns on block runs (see below); img is the
+// wave's run image, run_first the block's per-wave run words (block runs only).
+template <int R, bool NT, bool WT, bool O32, int WPB>
 __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& d, const Bases<R>& b, uint32_t lane,
-                                               lbyte* img, uint32_t main_region, uint32_t idx_region) {
+                                               uint32_t wave, lbyte* img, lptr<uint32_t> run_first,
+                                               uint32_t main_region, uint32_t idx_region) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
     uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
     if constexpr (NT) {
@@ -462,12 +466,10 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& 
             scale[i] = f ? t.s : s_exact;
         }
     }
+    // The four rows are one contiguous 2624-byte run (656 = 41 x 16): build it
+    // in the wave's LDS image and store it as 16-byte pieces, three wave-wide
+    // stores per replica instead of nine partial-line ones.
     if (d.run) {
-        // The four rows are one contiguous 2624-byte run (656 = 41 x 16): build
-        // it in the wave's LDS image and store it as 16-byte pieces, three
-        // wave-wide stores per replica instead of nine partial-line ones.
-        // Only this wave touches its image, and LDS accesses of one wave
-        // complete in order, so no barrier is needed.
 #pragma unroll
         for (int k = 0; k < 4; ++k) *(lptr<u32x2>)(img + k * 656u + lane * 8u) = codes[k];
         if ((lane & 15u) == 0) {
@@ -476,6 +478,40 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& 
                 *(lptr<uint32_t>)(img + k * 656u + 512u + (lane >> 4) * 4u) = __float_as_uint(scale[k]);
         }
         if (lane < 32u) *(lptr<u32x4>)(img + ((lane >> 3) & 3u) * 656u + 528u + (lane & 7u) * 16u) = G.rp;
+    }
+    bool block_run = false;
+    if constexpr (WPB > 4) {
+        // Block runs (launches of more than the L2s hold): when the block's WPB
+        // waves all hold runs and the runs follow each other in the Main-KV
+        // array (offsets base + w * 2624: consecutive slots, across a page
+        // boundary too when pages are dense), the block stores its WPB * 2624
+        // bytes as one run, every lane taking 16-byte pieces: longer bursts per
+        // replica than four 2624-byte runs written by different waves.  Every
+        // wave of the block reaches both barriers (no wave of a block returns
+        // early), and every wave reads the same WPB words, so the decision is
+        // the same in all of them.  Row offsets are multiples of 16, so the
+        // all-ones word (not a run) never matches an expected offset.
+        static_assert(O32, "block runs compare 32-bit offsets");
+        if (lane == 0) run_first[wave] = d.run ? (uint32_t)d.row[0] : ~0u;
+        __syncthreads();
+        const uint32_t r0 = run_first[0];
+        block_run = r0 != ~0u;
+#pragma unroll
+        for (uint32_t w = 1; w < (uint32_t)WPB; ++w) block_run = block_run && run_first[w] == r0 + w * kRunBytes;
+        if (block_run) {
+            const lbyte* bimg = img - wave * kRunBytes;   // the waves' images are contiguous
+            for (uint32_t pc = threadIdx.x; pc < (uint32_t)WPB * (kRunBytes / 16u); pc += (uint32_t)WPB * 64u) {
+                const u32x4 v = *(lptr<u32x4>)(bimg + pc * 16u);
+#pragma unroll
+                for (int r = 0; r < R; ++r) put_at<NT, WT, true>(b.main[r], main_region, r0 + pc * 16u, v);
+            }
+        }
+    }
+    if (block_run) {
+        // stored above, by the whole block
+    } else if (d.run) {
+        // Only this wave touches its image, and LDS accesses of one wave
+        // complete in order, so no barrier is needed.
         __builtin_amdgcn_wave_barrier();
         const u32x4 c0 = *(lptr<u32x4>)(img + lane * 16u);
         const u32x4 c1 = *(lptr<u32x4>)(img + 1024u + lane * 16u);
@@ -544,17 +580,23 @@ __device__ __forceinline__ void fetch_rows(const uint16_t* latent, const uint16_
 // instructions need: they arrive preloaded in SGPRs (kernel-argument
 // preloading); p is fetched while the row loads are in flight.  Token
 // indices are 32-bit (a launch holds at most kMaxTokensPerLaunch tokens).
-template <int R, bool NT, bool WT, bool O32>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
+template <int R, bool NT, bool WT, bool O32, int WPB>
+__global__ __launch_bounds__(WPB * 64) void store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
     uint32_t indexer_stride, const CtxHead* __restrict__ head, const StoreParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t run_img[kWavesPerBlock][kRunBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t run_img[WPB][kRunBytes];
+    __shared__ uint32_t run_first[WPB];
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t num_blocks = (num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;   // == gridDim.x
-    const uint32_t t0 = (xcd_chunk(blockIdx.x, num_blocks) * kWavesPerBlock + wave) * kTokensPerWave;
-    if (t0 >= num_tokens) return;
+    constexpr uint32_t kBlockTokens = kTokensPerWave * WPB;
+    const uint32_t num_blocks = (num_tokens + kBlockTokens - 1) / kBlockTokens;   // == gridDim.x
+    const uint32_t tb = xcd_chunk(blockIdx.x, num_blocks) * kBlockTokens;       // the block's first token
+    const uint32_t t0 = tb + wave * kTokensPerWave;
+    // With block runs every wave takes part in the block's barriers: a wave past
+    // the end of the batch carries on with no slot to store (its tokens are
+    // clamped to the last one and marked padded); only without them may it leave.
+    if ((WPB > 4 ? tb : t0) >= num_tokens) return;
     const uint32_t last = num_tokens - 1;
     // Scalar loads (slots, the status word and capacity) do not share a counter
     // with the row loads, so the destinations are worked out before the rows
@@ -580,7 +622,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void store_kernel(
     const Bases<R> b = pin_bases<R>(p);
     const Dest<O32> d = destinations<O32>(sl[0], sl[1], sl[2], sl[3], poisoned ? 0u : ok, lane, p);
     __builtin_amdgcn_sched_barrier(0);
-    quantize_store<R, NT, WT, O32>(G, d, b, lane, (lbyte*)&run_img[wave][0], p.main_region, p.idx_region);
+    quantize_store<R, NT, WT, O32, WPB>(G, d, b, lane, wave, (lbyte*)&run_img[wave][0],
+                                        (lptr<uint32_t>)&run_first[0], p.main_region, p.idx_region);
 }
 
 // Small batches (a decode step: tens of tokens; up to about a thousand).
@@ -684,20 +727,21 @@ __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
 
 }  // namespace
 
-template <bool NT, bool WT, bool O32>
-static void launch_r(uint32_t num_replicas, dim3 grid, dim3 block, hipStream_t stream, const uint16_t* lat,
+template <bool NT, bool WT, bool O32, int WPB>
+static void launch_r(uint32_t num_replicas, hipStream_t stream, const uint16_t* lat,
                      const uint16_t* rp, const uint16_t* ix, const int64_t* sl, uint32_t n, const StoreParams& p) {
+    const dim3 grid((n + kTokensPerWave * WPB - 1) / (kTokensPerWave * WPB)), block(WPB * 64);
 #define KVPUB_ROW_ARGS lat, rp, ix, sl, n, (uint32_t)p.latent_stride, (uint32_t)p.rope_stride, \
     (uint32_t)p.indexer_stride, p.head, p
     switch (num_replicas) {
-        case 1: store_kernel<1, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 2: store_kernel<2, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 3: store_kernel<3, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 4: store_kernel<4, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 5: store_kernel<5, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 6: store_kernel<6, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 7: store_kernel<7, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        default: store_kernel<8, NT, WT, O32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 1: store_kernel<1, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 2: store_kernel<2, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 3: store_kernel<3, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 4: store_kernel<4, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 5: store_kernel<5, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 6: store_kernel<6, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 7: store_kernel<7, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        default: store_kernel<8, NT, WT, O32, WPB><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
     }
 #undef KVPUB_ROW_ARGS
 }
@@ -731,8 +775,6 @@ hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t
     }
     for (int64_t t = 0; t < p.num_tokens; t += kMaxTokensPerLaunch) {
         const int64_t n = p.num_tokens - t < kMaxTokensPerLaunch ? p.num_tokens - t : kMaxTokensPerLaunch;
-        const uint32_t blocks = (uint32_t)((n + kTokensPerBlock - 1) / kTokensPerBlock);
-        const dim3 grid(blocks), block(kWavesPerBlock * 64);
         const uint16_t* lat = p.latent + t * p.latent_stride;
         const uint16_t* rp = p.rope + t * p.rope_stride;
         const uint16_t* ix = p.indexer + t * p.indexer_stride;
@@ -742,14 +784,15 @@ hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t
         // path's buffer stores need them)
         const bool offsets32 = p.main_region != 0 && p.idx_region != 0;
         const uint32_t un = (uint32_t)n;
+        // (launches over 32 MB: blocks of kBlockRunWaves waves with block runs)
         if (written <= kStreamingStoreBytes) {
-            if (offsets32) launch_r<true, false, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
-            else launch_r<true, false, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+            if (offsets32) launch_r<true, false, true, kWavesPerBlock>(num_replicas, stream, lat, rp, ix, sl, un, p);
+            else launch_r<true, false, false, kWavesPerBlock>(num_replicas, stream, lat, rp, ix, sl, un, p);
         } else if (written > kWriteThroughBytes && offsets32) {
-            launch_r<false, true, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+            launch_r<false, true, true, kBlockRunWaves>(num_replicas, stream, lat, rp, ix, sl, un, p);
         } else {
-            if (offsets32) launch_r<false, false, true>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
-            else launch_r<false, false, false>(num_replicas, grid, block, stream, lat, rp, ix, sl, un, p);
+            if (offsets32) launch_r<false, false, true, kWavesPerBlock>(num_replicas, stream, lat, rp, ix, sl, un, p);
+            else launch_r<false, false, false, kWavesPerBlock>(num_replicas, stream, lat, rp, ix, sl, un, p);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

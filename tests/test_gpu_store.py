@@ -580,3 +580,52 @@ def test_fused_fanout_equals_per_replica_stores(orc, T):
         fused.free()
         for sc in singles:
             sc.free()
+
+
+@pytest.mark.parametrize("R,guard", [(4, 0), (3, 0), (4, 64)])
+def test_block_runs_of_large_launches(orc, R, guard):
+    """Launches writing more than 32 MB store a block's 32 rows as one run when the
+    block's eight groups are consecutive in the Main-KV array.  Dense pages (no guard:
+    a run continues across a page boundary) and guarded pages (it cannot); block runs
+    aligned and misaligned to the 32-token blocks; runs broken by a padded or an invalid
+    slot, by a jump, by a page boundary; scattered groups; a ragged tail.  Whole buffers
+    against the oracle, the invalid count."""
+    rng = np.random.default_rng(71 + R + guard)
+    T = (32 << 20) // (R * 788) + 4 * 32 + 13
+    num_pages = 3 * ((T + 63) // 64) + 8
+    layout = CacheLayout(replicas=R, layers=1, num_pages=num_pages, guard=guard)
+    cap = layout.capacity
+    slots = np.empty(T, np.int64)
+    upper = rng.permutation(np.arange(cap // 2, cap))   # scattered slots, drawn without repeats
+    pos, nxt, k, u = 0, 0, 0, 0
+    while pos < T:
+        kind = k % 6
+        k += 1
+        n = min(T - pos, [96, 64, 40, 33, 20, 128][kind])
+        if kind == 4:                               # scattered: slots from the top half of the cache
+            slots[pos:pos + n] = upper[u:u + n]
+            u += n
+        else:                                       # a run starting where the previous one ended (+ a skip)
+            start = nxt + [0, 5, 64 - 7, 3, 0, 16][kind]
+            slots[pos:pos + n] = start + np.arange(n)
+            nxt = start + n
+        pos += n
+    assert nxt < cap // 2, "runs overran the lower half"
+    # distinct slots (scattered picks are from the upper half), then breaks inside runs
+    slots[np.arange(300, T, 997)] = -1
+    slots[[45, 2000, T - 40]] = [cap + 1, 3 * cap, -5]
+    assert np.unique(slots[slots >= 0]).size == np.count_nonzero(slots >= 0)
+    lat, rope, ind = W._normal_rows(rng, T)
+    x = LayerInputs(lat, rope, ind, slots)
+    G.log(f"block runs: R={R} guard={guard} T={T} pages={num_pages}")
+    dev = G.DeviceCache(layout)
+    try:
+        kvpub.check(dev.store(0, G.DeviceInputs(x)), "kvpub_store")
+        st, invalid, flags = dev.errors()
+        kvpub.check(st, "kvpub_error_read")
+        assert invalid == 3 and flags == 0
+        mains, idxs, inv = G.oracle_replicas(orc, layout, [(0, x)])
+        assert inv == 3
+        G.assert_full_parity(dev, mains, idxs)
+    finally:
+        dev.free()
