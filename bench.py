@@ -180,8 +180,6 @@ def main():
     kvpub.check(st)
     assert invalid == 0 and flags == 0
     tokens_per_s = valid * L / (step_ms * 1e-3)
-    log("verifying the timed steps' output")
-    check = verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer=L // 2)
 
     def graph_us(body, reps):
         """Average microseconds per replay of a torch graph of body()."""
@@ -255,6 +253,10 @@ def main():
                "at the value published at capture however often the graph is replayed",
     }
 
+    # what the timed steps wrote (the later graphs of this section wrote the same bytes again)
+    log("verifying the timed steps' output")
+    check = verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer=L // 2)
+
     gather = None if args.no_extras else gather_line(torch, kvpub, ctx, slots, T, valid, stream)
     floor_graph = None if args.no_extras else floor_graph_layer(torch, stream, L, valid, R, store_us)
 
@@ -289,7 +291,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "store_kernel<2, true, false, true>",
+            "kernel": "store_kernel<2, true, false, true, 4>",
             "achieved": round(store_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -347,7 +349,8 @@ def written_offsets(torch, layout, layer, slots_np):
 
 
 def verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer):
-    """After the timed replays: every replica equals replica 0 (whole buffers); in
+    """After the graph workload's timing legs (which all write the bytes the timed
+    steps wrote): every replica equals replica 0 (whole buffers); in
     `layer`, every byte outside the written rows still holds the fill pattern; the
     end canaries are intact.  (The written bytes are compared with the CPU oracle in
     the cpu_baseline leg, which runs the oracle on the same inputs.)"""
@@ -367,7 +370,7 @@ def verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer):
     for buf in main_bufs + idx_bufs:
         assert bool((buf[-CANARY_BYTES:] == GUARD).all()), "end-of-buffer canary changed"
     return {"replicas_identical": True, "untouched_bytes_layer": layer, "rows_written_per_layer": int(valid.sum()),
-            "how": "after the timed replays: torch.equal of every replica with replica 0, every byte outside one "
+            "how": "after the graph workload's timing legs: torch.equal of every replica with replica 0, every byte outside one "
                    "layer's written rows against the fill pattern, the end canaries; the CPU oracle's bytes for "
                    "the last layer are compared in cpu_baseline (oracle_layer_check)"}
 
