@@ -61,6 +61,7 @@ constexpr uint32_t kRunBytes = 4 * 656;   // 2624 = 164 x 16 B
 constexpr int64_t kCacheBytesPerToken = 656 + 128 + 4;              // per replica
 constexpr int64_t kStreamingStoreBytes = int64_t(16) << 20;         // launches writing at most this stream
 constexpr int64_t kWriteThroughBytes = int64_t(32) << 20;           // more than the 8 L2s hold: write through
+constexpr int64_t kMaxStride32 = int64_t(1) << 28;                  // input row stride (elements): 32-bit loads
 constexpr int kBlockRunWaves = 8;   // waves per block of those launches (block runs of 32 rows, 20,992 bytes)
 // Batches up to this many tokens take small_store_kernel (up to twice as many
 // with one or two replicas): measured crossover against the main kernel.
@@ -550,6 +551,49 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& 
     }
 }
 
+// Row loads with 32-bit lane offsets, for the streamed launches (one wave per
+// SIMD at the graph-layer size, where a wave's time to its first load is on
+// the launch's critical path): each load is a uniform base in SGPRs plus a
+// 32-bit offset per lane, the form the load instruction takes as is, so the
+// six loads leave after a few 32-bit operations instead of 64-bit address
+// arithmetic per lane (graph layer 3.99 -> 3.89 us; the write-back launches,
+// with two waves per SIMD, lose 3 % with it and keep fetch_rows).  The four
+// latent rows share one base (the group's first token, clamped to the batch)
+// and add the row's distance in bytes; the RoPE and Indexer-K pieces take
+// their lane's token the same way.  Needs every row stride at most
+// kMaxStride32 elements (checked on the host): the largest offset,
+// 3 rows x 2 B x stride + 1008, then stays below 2^32.
+typedef __attribute__((address_space(1))) const uint8_t cgbyte;   // a byte of a global input
+
+__device__ __forceinline__ u32x4 ld16_at(cgbyte* base, uint32_t off) {
+    return __builtin_nontemporal_load((__attribute__((address_space(1))) const u32x4*)(base + off));
+}
+
+// Keep a uniform 64-bit input address in SGPRs: without the pin the compiler
+// folds the lane offset into a 64-bit per-lane address.
+__device__ __forceinline__ cgbyte* uniform_base(const uint16_t* p) {
+    cgbyte* q = (cgbyte*)p;
+    asm volatile("" : "+s"(q));
+    return q;
+}
+
+__device__ __forceinline__ void fetch_rows32(const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
+                                             uint32_t latent_stride, uint32_t rope_stride, uint32_t indexer_stride,
+                                             uint32_t t0, uint32_t last, uint32_t lane, Group& G) {
+    const uint32_t tb = t0 < last ? t0 : last;
+    const uint32_t ur = t0 + ((lane >> 3) & 3u), ug = t0 + (lane >> 4);
+    const uint32_t kr = (ur < last ? ur : last) - tb, kg = (ug < last ? ug : last) - tb;
+    G.rp = ld16_at(uniform_base(rope + (uint64_t)tb * rope_stride), kr * (rope_stride * 2u) + (lane & 7u) * 16u);
+    cgbyte* lb = uniform_base(latent + (uint64_t)tb * latent_stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t t = t0 + k < last ? t0 + k : last;
+        G.lat[k] = ld16_at(lb, (t - tb) * (latent_stride * 2u) + lane * 16u);
+    }
+    G.ix = ld16_at(uniform_base(indexer + (uint64_t)tb * indexer_stride),
+                   kg * (indexer_stride * 2u) + (lane & 15u) * 16u);
+}
+
 // Slots of the group starting at token t0 (scalar loads).  Token indices
 // past the end are clamped to the last token (always in bounds).
 __device__ __forceinline__ void fetch_slots(const int64_t* __restrict__ slots, uint32_t t0, uint32_t last,
@@ -600,12 +644,22 @@ __global__ __launch_bounds__(WPB * 64) void store_kernel(
     const uint32_t last = num_tokens - 1;
     // Scalar loads (slots, the status word and capacity) do not share a counter
     // with the row loads, so the destinations are worked out before the rows
-    // arrive.
+    // arrive.  In streamed launches with 32-bit offsets the row loads leave
+    // first: they have the longer way to go, and their addresses need no
+    // scalar load.
     int64_t sl[4];
-    fetch_slots(slots, t0, last, sl);
-    const CtxHead h = *head;
     Group G;
-    fetch_rows(latent, rope, indexer, latent_stride, rope_stride, indexer_stride, t0, last, lane, G);
+    CtxHead h;
+    if constexpr (O32 && NT) {
+        fetch_rows32(latent, rope, indexer, latent_stride, rope_stride, indexer_stride, t0, last, lane, G);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_slots(slots, t0, last, sl);
+        h = *head;
+    } else {
+        fetch_slots(slots, t0, last, sl);
+        h = *head;
+        fetch_rows(latent, rope, indexer, latent_stride, rope_stride, indexer_stride, t0, last, lane, G);
+    }
     __builtin_amdgcn_sched_barrier(0);
     const bool poisoned = (h.status & kStatusPoisoned) != 0;  // a fence timed out: fail closed
     // Slots of tokens past the end become -1; invalid slots (neither -1 nor a
@@ -781,12 +835,16 @@ hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t
         const int64_t* sl = p.slots + t;
         const int64_t written = n * (int64_t)num_replicas * kCacheBytesPerToken;
         // every layer spans less than 4 GiB: 32-bit offsets (the write-through
-        // path's buffer stores need them)
+        // path's buffer stores need them); streamed launches also load with
+        // 32-bit offsets, which needs input rows at most kMaxStride32 elements apart
         const bool offsets32 = p.main_region != 0 && p.idx_region != 0;
+        const bool loads32 = p.latent_stride <= kMaxStride32 && p.rope_stride <= kMaxStride32 &&
+                             p.indexer_stride <= kMaxStride32;
         const uint32_t un = (uint32_t)n;
         // (launches over 32 MB: blocks of kBlockRunWaves waves with block runs)
         if (written <= kStreamingStoreBytes) {
-            if (offsets32) launch_r<true, false, true, kWavesPerBlock>(num_replicas, stream, lat, rp, ix, sl, un, p);
+            if (offsets32 && loads32)
+                launch_r<true, false, true, kWavesPerBlock>(num_replicas, stream, lat, rp, ix, sl, un, p);
             else launch_r<true, false, false, kWavesPerBlock>(num_replicas, stream, lat, rp, ix, sl, un, p);
         } else if (written > kWriteThroughBytes && offsets32) {
             launch_r<false, true, true, kBlockRunWaves>(num_replicas, stream, lat, rp, ix, sl, un, p);
