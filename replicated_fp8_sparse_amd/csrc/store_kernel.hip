@@ -68,19 +68,21 @@ constexpr int kBlockRunWaves = 8;   // waves per block of those launches (block 
 constexpr int64_t kSmallBatchTokens = 1024;
 
 // Store policy by launch size:
-//   NT (a launch writing at most kStreamingStoreBytes): the pieces made of
-//     whole lines (row runs -- all but one edge line of a 2624-byte run -- and
-//     Indexer-K codes) are stored non-temporally, the partial pieces (scales,
-//     the per-row path) with ordinary write-back stores.  Nothing of the whole lines is left dirty in
-//     L2 for the end-of-kernel write-back, which a latency-bound launch would
-//     otherwise wait for, while the partial lines still merge in L2.
+//   NT (a launch writing at most kStreamingStoreBytes): the whole-line kind of
+//     pieces (row runs, which cover whole 128-byte lines apart from the lines at
+//     their two ends, and Indexer-K codes) are stored non-temporally, the
+//     partial pieces (scales, the per-row path) with ordinary write-back
+//     stores.  The whole lines are then not left dirty in L2 for the
+//     end-of-kernel write-back, which a latency-bound launch would otherwise
+//     wait for, while the partial lines still merge in L2.
 //   WT (a launch writing more than kWriteThroughBytes, more than the eight
 //     4 MB L2s can hold): the whole-line pieces are buffer stores with the
 //     device-coherence bit, written through this XCD's L2 instead of held
 //     dirty in it, so the writes stream out while the kernel runs instead of
-//     being evicted later; the partial pieces (the 16-byte Indexer-K scale
-//     runs, four waves to a 64-byte line) stay write-back, so they merge in
-//     L2 instead of reaching memory as partial writes.  Buffer offsets are
+//     being evicted later; the partial pieces (the per-row path, and the
+//     16-byte Indexer-K scale runs, eight waves to a 128-byte line) stay
+//     write-back, so they merge in L2 instead of reaching memory as partial
+//     writes.  Buffer offsets are
 //     32-bit, so WT needs each replica's layer to span less than 2^32 bytes;
 //     the buffer's range check (num_records = the layer's span) drops any
 //     whole-line store outside the layer.
@@ -272,8 +274,6 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// Where a group's pieces go, worked out from the slots while its rows are in
-// flight.  Offsets are bytes from a replica's layer base.
 // Replica layer bases, held in SGPRs for the whole wave.
 template <int R>
 struct Bases {
@@ -285,6 +285,8 @@ struct Bases {
 // 4 GiB (O32), else 64-bit.
 template <bool O32> using Off = typename std::conditional<O32, uint32_t, uint64_t>::type;
 
+// Where a group's pieces go, worked out from the slots while its rows are in
+// flight.  Offsets are bytes from a replica's layer base.
 template <bool O32>
 struct Dest {
     Off<O32> row[4];   // Main-KV row of token k (wave-uniform)
@@ -416,7 +418,7 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& 
     if constexpr (NT) {
         // Launches of this size hold few waves per SIMD, so the unpacked values
         // may stay live from here to the quotients: the in-lane maximum comes
-        // from them (three max3 of magnitudes instead of eight packed steps).
+        // from them (four max3 of magnitudes instead of the packed steps).
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             float x[8];
