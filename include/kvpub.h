@@ -101,7 +101,8 @@ typedef enum {
     KVPUB_OK = 0,
     KVPUB_ERR_INVALID_ARG = 1,   /* bad argument; nothing was launched */
     KVPUB_ERR_OUT_OF_MEMORY = 2, /* an allocation failed; nothing is left allocated */
-    KVPUB_ERR_UNSUPPORTED = 3,   /* device is not gfx950 */
+    KVPUB_ERR_UNSUPPORTED = 3,   /* device is not gfx950, or the call does not support this
+                                    configuration (documented per call) */
     KVPUB_ERR_HIP = 4,           /* a HIP runtime call failed */
     KVPUB_ERR_CAPTURING = 5,     /* a synchronizing call while a stream capture is active */
     KVPUB_ERR_FENCE_TIMEOUT = 6, /* a fence timed out: the context is poisoned */

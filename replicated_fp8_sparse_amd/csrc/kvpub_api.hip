@@ -646,7 +646,7 @@ KVPUB_API const char* kvpub_strerror(kvpub_status s) {
         case KVPUB_OK: return "ok";
         case KVPUB_ERR_INVALID_ARG: return "invalid argument";
         case KVPUB_ERR_OUT_OF_MEMORY: return "out of memory";
-        case KVPUB_ERR_UNSUPPORTED: return "unsupported device (needs gfx950)";
+        case KVPUB_ERR_UNSUPPORTED: return "not supported (device not gfx950, or a configuration this call does not take)";
         case KVPUB_ERR_HIP: return "HIP runtime error";
         case KVPUB_ERR_CAPTURING: return "synchronizing call during stream capture";
         case KVPUB_ERR_FENCE_TIMEOUT: return "fence timed out; context poisoned";
