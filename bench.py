@@ -8,8 +8,8 @@ wait on the epoch), so every part of the hot path runs: slot decode, row
 loads, tile amax, scale, e4m3 quantization, row packing, the R-way fan-out
 stores, the fence, graph replay.  Inputs are seeded N(0,1) bf16 rows already
 resident in HBM; the cache layout is the one the library documents (656-byte
-Main-KV rows, 8448-byte Indexer-K pages).  After the timed replays the
-replicas are checked for identity and one layer against the CPU oracle.
+Main-KV rows, 8448-byte Indexer-K pages).  After the graph workload's timing
+legs the replicas are checked for identity and one layer against the CPU oracle.
 
 Printed: one JSON line with tokens/s (value), the store kernel's achieved HBM
 bandwidth against the 8 TB/s peak (roofline), the fence cost per layer in its
