@@ -237,6 +237,43 @@ def test_ragged_and_strided(orc, T, mapping):
         dev.free()
 
 
+@pytest.mark.parametrize("R,T", [(1, 2049), (2, 2050), (2, 2051), (1, 3003), (2, 4095)])
+def test_streamed_launch_ragged_real_tokens(orc, R, T):
+    """Streamed launches (at most 16 MB written, 32-bit offsets: the graph layer's
+    path, whose row loads use per-group bases and 32-bit lane offsets) with a
+    token count that leaves the last group short, every token real (no padding
+    after it), rows wider than their data, into the second of two layers; a few
+    pads and invalid slots among them."""
+    import torch
+    rng = np.random.default_rng(700 + T)
+    layout = CacheLayout(replicas=R, layers=2, num_pages=72)
+    LS, RS, IS = 528, 80, 144
+    wide_l = bf16_bits(rng.standard_normal((T, LS)).astype(np.float32))
+    wide_r = bf16_bits(rng.standard_normal((T, RS)).astype(np.float32))
+    wide_i = bf16_bits(rng.standard_normal((T, IS)).astype(np.float32))
+    slots = rng.permutation(layout.capacity)[:T].astype(np.int64)
+    slots[rng.choice(T - 8, T // 20, replace=False)] = -1               # pads, not in the last group
+    slots[rng.choice(T - 8, 3, replace=False)] = layout.capacity + 5    # invalid, counted
+    assert (slots[-(T % 4):] >= 0).all()
+    x = LayerInputs(np.ascontiguousarray(wide_l[:, :512]), np.ascontiguousarray(wide_r[:, :64]),
+                    np.ascontiguousarray(wide_i[:, :128]), slots)
+    G.log(f"streamed ragged R={R} T={T} strides {LS}/{RS}/{IS}, layer 1 of 2")
+    assert T * R * 788 <= 16 << 20
+    dev = G.DeviceCache(layout)
+    try:
+        dl, dr, di = G.to_dev_u16(wide_l), G.to_dev_u16(wide_r), G.to_dev_u16(wide_i)
+        ds = G.to_dev_i64(slots)
+        kvpub.check(kvpub.kvpub_store(dev.ctx, 1, T, dl.data_ptr(), LS, dr.data_ptr(), RS, di.data_ptr(),
+                                      IS, ds.data_ptr(), torch.cuda.current_stream().cuda_stream), "kvpub_store")
+        st, invalid, flags = dev.errors()
+        kvpub.check(st, "kvpub_error_read")
+        mains, idxs, want_invalid = G.oracle_replicas(orc, layout, [(1, x)])
+        assert invalid == want_invalid == 3 and flags == 0
+        G.assert_full_parity(dev, mains, idxs)
+    finally:
+        dev.free()
+
+
 def test_empty_store_is_noop(orc):
     layout = CacheLayout(replicas=2, layers=1, num_pages=2)
     dev = G.DeviceCache(layout)
