@@ -258,7 +258,7 @@ def main():
     check = verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer=L // 2)
 
     gather = None if args.no_extras else gather_line(torch, kvpub, ctx, slots, T, valid, stream)
-    floor_graph = None if args.no_extras else floor_graph_layer(torch, stream, L, valid, R, store_us)
+    floor_graph = None if args.no_extras else floor_graph_layer(torch, stream, L, T, valid, R, store_us)
 
     extras = {}
     decode = fanout = None
@@ -415,9 +415,40 @@ def floor_line(torch, stream, valid, R, n, store_us):
                    "policy"}
 
 
-def floor_graph_layer(torch, stream, L, valid, R, store_us):
+def empty_node_us(torch, stream, n, blocks, threads, reps=8):
+    """Average microseconds per node of a replayed graph of n empty-kernel launches."""
+    from replicated_fp8_sparse_amd import floor as fl
+    sh = stream.cuda_stream
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(n):
+                rc = fl.kvpub_floor_empty(blocks, threads, sh)
+                assert rc == 0, rc
+        g.replay()
+        with Timer(torch, stream) as t:
+            for _ in range(reps):
+                g.replay()
+    del g
+    return t.ms * 1e3 / (reps * n)
+
+
+def floor_graph_layer(torch, stream, L, T, valid, R, store_us):
+    """The floor for the graph layer's bytes, and the fixed cost of a launch of the
+    store's shape (an empty kernel with its grid, per graph node)."""
     log("floor for the graph layer")
-    return floor_line(torch, stream, valid, R, L, store_us)
+    out = floor_line(torch, stream, valid, R, L, store_us)
+    empty = empty_node_us(torch, stream, L, (T + 15) // 16, 256)
+    b = alg_bytes(valid, R)
+    out["empty_node_us"] = round(empty, 3)
+    out["store_less_empty_node_gbps"] = round(b / ((store_us - empty) * 1e-6) / 1e9, 1)
+    out["frac_cap_at_this_size"] = round(b / ((empty + b / (HBM_PEAK_GBPS * 1e9) * 1e6) * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+    out["empty_how"] = (f"a replayed graph of {L} launches of an empty kernel with the store's grid "
+                        f"({(T + 15) // 16} blocks of 256 threads): the fixed cost of each graph node; "
+                        "store_less_empty_node_gbps = algorithmic bytes / (store time - that cost); "
+                        "frac_cap_at_this_size = the fraction of peak a launch of these bytes would reach if its "
+                        "work took exactly bytes / peak on top of the fixed cost")
+    return out
 
 
 def store_only_extras(torch, kvpub, W, stream):

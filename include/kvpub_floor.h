@@ -12,7 +12,8 @@
  * every replica); timing this kernel with in_bytes = T x 1408 and R outputs of
  * T x 788 bytes gives the achievable time for the store's bytes.  Each output
  * piece holds the input piece of the same index (pieces past the input's end
- * hold their own index in every word).
+ * hold their own index in every word).  A second entry point launches an
+ * empty kernel, the fixed per-launch cost.
  */
 #ifndef KVPUB_FLOOR_H
 #define KVPUB_FLOOR_H
@@ -42,6 +43,14 @@ extern "C" {
  * the launch failed.  No allocation, no synchronization. */
 KVPUB_FLOOR_API int kvpub_floor_stream(const void *in, uint64_t in_bytes, void *const *outs, uint32_t n_outs,
                                        uint64_t out_bytes, uint32_t policy, void *stream);
+
+/* Enqueue one launch of an empty kernel (no instruction but the end) with
+ * `blocks` (1..2^31-1) blocks of `threads` (64..1024, a multiple of 64)
+ * threads on `stream`: the fixed cost of a launch of that shape, which a
+ * replayed graph of such launches measures per node.  Returns 0 when
+ * launched, 1 for an invalid argument (nothing launched), 4 if the launch
+ * failed. */
+KVPUB_FLOOR_API int kvpub_floor_empty(uint32_t blocks, uint32_t threads, void *stream);
 
 #ifdef __cplusplus
 }

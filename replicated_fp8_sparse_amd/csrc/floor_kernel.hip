@@ -1,4 +1,5 @@
-// Plain-stream floor kernel (measurement only; see include/kvpub_floor.h).
+// Plain-stream floor kernel and an empty kernel (measurement only; see
+// include/kvpub_floor.h).
 //
 // One 16-byte piece per lane: lane i loads input piece i (non-temporal) and
 // stores it to output piece i of every output buffer.  Lanes past the output
@@ -63,6 +64,9 @@ void launch_n(uint32_t n, dim3 grid, hipStream_t s, const u32x4* in, uint64_t pi
     }
 }
 
+// Nothing but the end of the program: the cost of a launch as such.
+__global__ void empty_kernel() {}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
@@ -90,5 +94,12 @@ extern "C" KVPUB_FLOOR_API int kvpub_floor_stream(const void* in, uint64_t in_by
     if (policy == KVPUB_FLOOR_WRITE_BACK) launch_n<KVPUB_FLOOR_WRITE_BACK>(n_outs, grid, s, src, pin, o, pout);
     else if (policy == KVPUB_FLOOR_NON_TEMPORAL) launch_n<KVPUB_FLOOR_NON_TEMPORAL>(n_outs, grid, s, src, pin, o, pout);
     else launch_n<KVPUB_FLOOR_WRITE_THROUGH>(n_outs, grid, s, src, pin, o, pout);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+extern "C" KVPUB_FLOOR_API int kvpub_floor_empty(uint32_t blocks, uint32_t threads, void* stream) {
+    if (blocks < 1 || blocks > 0x7FFFFFFFu || threads < 64 || threads > 1024 || threads % 64) return 1;
+    (void)hipGetLastError();
+    empty_kernel<<<dim3(blocks), dim3(threads), 0, static_cast<hipStream_t>(stream)>>>();
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }

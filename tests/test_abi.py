@@ -187,3 +187,8 @@ def test_floor_library_exports_its_header():
     assert f(8, 16, [16], 16, 0) == 1                      # misaligned
     assert f(16, 16, [16], 16, 3) == 1                     # unknown policy
     assert f(16, 16, [16], 1 << 32, floor.KVPUB_FLOOR_WRITE_THROUGH) == 1   # 32-bit buffer offsets
+    e = floor.kvpub_floor_empty
+    assert e(0, 64) == 1                                   # no block
+    assert e(1, 32) == 1 and e(1, 100) == 1                # not a multiple of 64 threads
+    assert e(1, 2048) == 1                                 # more than 1024 threads
+    assert e(1 << 31, 64) == 1                             # grid too large

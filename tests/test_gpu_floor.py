@@ -28,3 +28,16 @@ def test_floor_stream_bytes(policy, in_bytes, out_bytes, n_outs):
         want[in_bytes:] = np.repeat(idx, 4).view(np.uint8)
     for o in outs:
         assert np.array_equal(o.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("blocks,threads", [(1, 64), (256, 256), (1024, 1024)])
+def test_floor_empty_launches(blocks, threads):
+    """The empty kernel launches with the documented shapes and leaves the stream usable."""
+    import torch
+    print(f"[gpu-test] floor empty {blocks}x{threads}", flush=True)
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        assert floor.kvpub_floor_empty(blocks, threads, s) == 0
+    torch.cuda.synchronize()
+    x = torch.arange(8, device="cuda")
+    assert int(x.sum()) == 28
