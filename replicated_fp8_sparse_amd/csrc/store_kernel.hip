@@ -399,14 +399,75 @@ __device__ __forceinline__ Dest<O32> destinations(int64_t s0, int64_t s1, int64_
     return d;
 }
 
+// Rounds B..B+N-1 of a group: codes and scales of their tiles.  Each lane of
+// DPP row j ends with the amax of the row's N tiles, so lane 16j + i takes tile
+// (round B + i, row j) and one scale sequence covers the N rounds' tiles (lanes
+// 16j + N.. repeat round B's tile).  UNPACKED: the in-lane maximum from the
+// unpacked values, which may then stay live until the quotients (launches of
+// few waves per SIMD: four max3 of magnitudes instead of the packed steps);
+// else from the packed bf16 bits.
+template <int B, int N, bool UNPACKED>
+__device__ __forceinline__ void quantize_rounds(const u32x4 (&rows)[5], u32x2 (&codes)[5], float (&scale)[5]) {
+    uint32_t ab[N];  // bf16 magnitude bits of each tile's amax (row-uniform)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if constexpr (UNPACKED) {
+            float x[8];
+            unpack8(rows[B + i], x);
+            // the shift (an ordinary instruction) also stands between the asm
+            // result and the DPP reads, whose wait states are the compiler's
+            ab[i] = row_max16(__float_as_uint(lane_amax_f32(x)) >> 16);
+        } else {
+            ab[i] = row_max16(lane_amax_bits(rows[B + i]));
+        }
+    }
+    uint32_t mine = ab[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) mine = select_lane_in_row(kLaneInRowMask << i, ab[i], mine);
+    const uint32_t E = mine >> 7;
+    if (__all(E >= kFastMinExponent && E < 255u)) {
+        const TileScale t = tile_scale(mine);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float si = bcast_in_row(t.s, i), yi = bcast_in_row(t.y, i);
+            float x[8], q[8];
+            unpack8(rows[B + i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], si, yi);
+            codes[B + i] = cvt8(q);
+            scale[B + i] = si;
+        }
+    } else {
+        // some tile of these rounds has a tiny (possibly subnormal) scale or is
+        // all zeros: those tiles divide, the others take the fast path
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t Ei = ab[i] >> 7;
+            const bool f = Ei >= kFastMinExponent && Ei < 255u;
+            const TileScale t = tile_scale(ab[i]);
+            const float s_exact = __uint_as_float(ab[i] << 16) / kE4m3Max;
+            float x[8], q[8];
+            unpack8(rows[B + i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[e], t.s, t.y) : quotient_exact(x[e], s_exact);
+            codes[B + i] = cvt8(q);
+            scale[B + i] = f ? t.s : s_exact;
+        }
+    }
+}
+
 // Quantize a group and store every piece to each of the R replicas:
 //   codes of token k  -> row bytes [8*lane, +8)
 //   scale of tile j   -> row bytes [512 + 4j, +4)       (lane 16j)
 //   RoPE              -> row bytes [528 + 16*(lane%8), +16) of token lane/8 (lanes 0..31)
 //   Indexer-K codes   -> page bytes [128*(slot%64) + 8*(lane%16), +8) of token lane/16
 //   Indexer-K scale   -> page bytes [8192 + 4*(slot%64), +4) (lane 16g)
-// The five rounds are computed as one straight-line block (their reductions
-// and scale sequences interleave); only the stores are conditional.
+// Streamed launches (one wave per SIMD at the graph-layer size) quantize in
+// two phases: rounds 0-2 once their rows are in, while the last two rows are
+// still on their way (a wave's six rows come back over about 0.3 us), then
+// rounds 3-4; each phase's reductions and scale sequence interleave.  The
+// other launches, several waves per SIMD, take all five rounds in one block.
+// Only the stores are conditional.
 // WPB (waves per block) above 4 turns on block runs (see below); img is the
 // wave's run image, run_first the block's per-wave run words (block runs only).
 template <int R, bool NT, bool WT, bool O32, int WPB>
@@ -414,60 +475,14 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& 
                                                uint32_t wave, lbyte* img, lptr<uint32_t> run_first,
                                                uint32_t main_region, uint32_t idx_region) {
     const u32x4 rows[5] = {G.lat[0], G.lat[1], G.lat[2], G.lat[3], G.ix};
-    uint32_t ab[5];  // bf16 magnitude bits of each tile's amax (row-uniform)
-    if constexpr (NT) {
-        // Launches of this size hold few waves per SIMD, so the unpacked values
-        // may stay live from here to the quotients: the in-lane maximum comes
-        // from them (four max3 of magnitudes instead of the packed steps).
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            float x[8];
-            unpack8(rows[i], x);
-            // the shift (an ordinary instruction) also stands between the asm
-            // result and the DPP reads, whose wait states are the compiler's
-            ab[i] = row_max16(__float_as_uint(lane_amax_f32(x)) >> 16);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 5; ++i) ab[i] = row_max16(lane_amax_bits(rows[i]));
-    }
-    // Every lane of row j now holds the amax of all five of the row's tiles, so
-    // lane 16j + i takes tile (round i, row j) and one scale sequence covers
-    // the group's 20 tiles (lanes 16j + 5.. repeat round 0's tile).
-    uint32_t mine = ab[0];
-#pragma unroll
-    for (int i = 1; i < 5; ++i) mine = select_lane_in_row(kLaneInRowMask << i, ab[i], mine);
-    const uint32_t E = mine >> 7;
     u32x2 codes[5];
     float scale[5];
-    if (__all(E >= kFastMinExponent && E < 255u)) {
-        const TileScale t = tile_scale(mine);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const float si = bcast_in_row(t.s, i), yi = bcast_in_row(t.y, i);
-            float x[8], q[8];
-            unpack8(rows[i], x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = quotient_fast(x[e], si, yi);
-            codes[i] = cvt8(q);
-            scale[i] = si;
-        }
+    if constexpr (NT) {
+        quantize_rounds<0, 3, true>(rows, codes, scale);
+        __builtin_amdgcn_sched_barrier(0);
+        quantize_rounds<3, 2, true>(rows, codes, scale);
     } else {
-        // some tile of the wave has a tiny (possibly subnormal) scale or is all
-        // zeros: those tiles divide, the others take the fast path
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            const uint32_t E = ab[i] >> 7;
-            const bool f = E >= kFastMinExponent && E < 255u;
-            const TileScale t = tile_scale(ab[i]);
-            const float s_exact = __uint_as_float(ab[i] << 16) / kE4m3Max;
-            float x[8], q[8];
-            unpack8(rows[i], x);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) q[e] = f ? quotient_fast(x[e], t.s, t.y) : quotient_exact(x[e], s_exact);
-            codes[i] = cvt8(q);
-            scale[i] = f ? t.s : s_exact;
-        }
+        quantize_rounds<0, 5, false>(rows, codes, scale);
     }
     // The four rows are one contiguous 2624-byte run (656 = 41 x 16): build it
     // in the wave's LDS image and store it as 16-byte pieces, three wave-wide
