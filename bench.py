@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill / heavy-tail store-only figures")
+    ap.add_argument("--no-vmm", action="store_true",
+                    help="skip the heavy-tail store on VMM-backed replicas (hardware-counter passes use this)")
     ap.add_argument("--cpu-runs", type=int, default=5,
                     help="runs per CPU-baseline leg (the median is reported)")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -263,7 +265,7 @@ def main():
     extras = {}
     decode = fanout = None
     if not args.no_extras:
-        extras = store_only_extras(torch, kvpub, W, stream)
+        extras = store_only_extras(torch, kvpub, W, stream, vmm=not args.no_vmm)
         decode = decode_eager(torch, kvpub, W, stream)
         fanout = fanout_ab(torch, kvpub, W, stream)
 
@@ -451,7 +453,7 @@ def floor_graph_layer(torch, stream, L, T, valid, R, store_us):
     return out
 
 
-def store_only_extras(torch, kvpub, W, stream):
+def store_only_extras(torch, kvpub, W, stream, vmm=True):
     """Store-kernel bandwidth on the prefill (T=8192, R=4) and heavy-tail (T=32768, R=4)
     workloads.  Warm: a replayed graph of launches over rotated input copies and slot
     mappings that write disjoint page sets (16 prefill mappings in windows of 1024 pages,
@@ -462,8 +464,10 @@ def store_only_extras(torch, kvpub, W, stream):
     from replicated_fp8_sparse_amd import floor as _fl  # noqa: F401  (fails loudly if unbuilt)
     out = {}
     sh = stream.cuda_stream
-    for name, fn, vmm in (("prefill_T8192_R4", W.prefill, False), ("heavy_T32768_R4", W.heavy, False),
-                          ("heavy_T32768_R4_vmm", W.heavy, True)):
+    shapes = [("prefill_T8192_R4", W.prefill, False), ("heavy_T32768_R4", W.heavy, False)]
+    if vmm:
+        shapes.append(("heavy_T32768_R4_vmm", W.heavy, True))
+    for name, fn, vmm in shapes:
         layout, x = fn()
         rot = W.prefill_rotation_slots(16) if fn is W.prefill else W.heavy_rotation_slots(8)
         copies = len(rot)
