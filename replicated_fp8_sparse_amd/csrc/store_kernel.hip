@@ -479,6 +479,10 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& 
     float scale[5];
     if constexpr (NT) {
         quantize_rounds<0, 3, true>(rows, codes, scale);
+        if (d.run) {   // rows 0-2 of the run image (below) while rows 3 and 4 are on their way
+#pragma unroll
+            for (int k = 0; k < 3; ++k) *(lptr<u32x2>)(img + k * 656u + lane * 8u) = codes[k];
+        }
         __builtin_amdgcn_sched_barrier(0);
         quantize_rounds<3, 2, true>(rows, codes, scale);
     } else {
@@ -489,7 +493,7 @@ __device__ __forceinline__ void quantize_store(const Group& G, const Dest<O32>& 
     // stores per replica instead of nine partial-line ones.
     if (d.run) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *(lptr<u32x2>)(img + k * 656u + lane * 8u) = codes[k];
+        for (int k = NT ? 3 : 0; k < 4; ++k) *(lptr<u32x2>)(img + k * 656u + lane * 8u) = codes[k];
         if ((lane & 15u) == 0) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
