@@ -604,13 +604,16 @@ __device__ __forceinline__ void fetch_rows32(const uint16_t* latent, const uint1
     const uint32_t tb = t0 < last ? t0 : last;
     const uint32_t ur = t0 + ((lane >> 3) & 3u), ug = t0 + (lane >> 4);
     const uint32_t kr = (ur < last ? ur : last) - tb, kg = (ug < last ? ug : last) - tb;
-    G.rp = ld16_at(uniform_base(rope + (uint64_t)tb * rope_stride), kr * (rope_stride * 2u) + (lane & 7u) * 16u);
+    // in order of first use by the two quantization phases: latent rows 0-2,
+    // then row 3, the RoPE piece (first needed when the run image is built)
+    // and the Indexer-K row
     cgbyte* lb = uniform_base(latent + (uint64_t)tb * latent_stride);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const uint32_t t = t0 + k < last ? t0 + k : last;
         G.lat[k] = ld16_at(lb, (t - tb) * (latent_stride * 2u) + lane * 16u);
     }
+    G.rp = ld16_at(uniform_base(rope + (uint64_t)tb * rope_stride), kr * (rope_stride * 2u) + (lane & 7u) * 16u);
     G.ix = ld16_at(uniform_base(indexer + (uint64_t)tb * indexer_stride),
                    kg * (indexer_stride * 2u) + (lane & 15u) * 16u);
 }
