@@ -714,7 +714,11 @@ __global__ __launch_bounds__(WPB * 64) void store_kernel(
 // batches the main kernel's merged run stores win).
 constexpr int kSmallWaves = 5;
 
-template <int R>
+// L32: the rows are loaded from SGPR bases with 32-bit lane offsets (as in
+// fetch_rows32; needs the Indexer-K row stride at most kMaxStride32
+// elements), after the slot loads: with so few blocks the slots and the
+// offsets that depend on them are the longer chain, so they leave first.
+template <int R, bool L32>
 __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
     const uint16_t* latent, const uint16_t* rope, const uint16_t* indexer,
     const int64_t* __restrict__ slots, uint32_t num_tokens, uint32_t latent_stride, uint32_t rope_stride,
@@ -727,13 +731,26 @@ __global__ __launch_bounds__(kSmallWaves * 64) void small_store_kernel(
     fetch_slots(slots, t0, last, sl);
     const CtxHead h = *head;
     u32x4 row, rp = u32x4{0u, 0u, 0u, 0u};
-    if (round < 4) {
-        const uint32_t t = t0 + round < last ? t0 + round : last;
-        rp = ld16(rope + (uint64_t)t * rope_stride + (lane & 7u) * 8u);
-        row = ld16(latent + (uint64_t)t * latent_stride + lane * 8u);
+    if constexpr (L32) {
+        if (round < 4) {
+            const uint32_t t = t0 + round < last ? t0 + round : last;
+            rp = ld16_at(uniform_base(rope + (uint64_t)t * rope_stride), (lane & 7u) * 16u);
+            row = ld16_at(uniform_base(latent + (uint64_t)t * latent_stride), lane * 16u);
+        } else {
+            const uint32_t tb = t0 < last ? t0 : last, ug = t0 + (lane >> 4);
+            const uint32_t kg = (ug < last ? ug : last) - tb;
+            row = ld16_at(uniform_base(indexer + (uint64_t)tb * indexer_stride),
+                          kg * (indexer_stride * 2u) + (lane & 15u) * 16u);
+        }
     } else {
-        const uint32_t ug = t0 + (lane >> 4), tg = ug < last ? ug : last;
-        row = ld16(indexer + (uint64_t)tg * indexer_stride + (lane & 15u) * 8u);
+        if (round < 4) {
+            const uint32_t t = t0 + round < last ? t0 + round : last;
+            rp = ld16(rope + (uint64_t)t * rope_stride + (lane & 7u) * 8u);
+            row = ld16(latent + (uint64_t)t * latent_stride + lane * 8u);
+        } else {
+            const uint32_t ug = t0 + (lane >> 4), tg = ug < last ? ug : last;
+            row = ld16(indexer + (uint64_t)tg * indexer_stride + (lane & 15u) * 8u);
+        }
     }
     const bool poisoned = (h.status & kStatusPoisoned) != 0;
     uint32_t nbad = 0, tok = 0;
@@ -824,21 +841,27 @@ static void launch_r(uint32_t num_replicas, hipStream_t stream, const uint16_t* 
 #undef KVPUB_ROW_ARGS
 }
 
-static void launch_small(uint32_t num_replicas, uint32_t n, hipStream_t stream, const StoreParams& p) {
+template <bool L32>
+static void launch_small_l(uint32_t num_replicas, uint32_t n, hipStream_t stream, const StoreParams& p) {
     const dim3 grid((n + kTokensPerWave - 1) / kTokensPerWave), block(kSmallWaves * 64);
 #define KVPUB_ROW_ARGS p.latent, p.rope, p.indexer, p.slots, n, (uint32_t)p.latent_stride, \
     (uint32_t)p.rope_stride, (uint32_t)p.indexer_stride, p.head, p
     switch (num_replicas) {
-        case 1: small_store_kernel<1><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 2: small_store_kernel<2><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 3: small_store_kernel<3><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 4: small_store_kernel<4><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 5: small_store_kernel<5><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 6: small_store_kernel<6><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        case 7: small_store_kernel<7><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
-        default: small_store_kernel<8><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 1: small_store_kernel<1, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 2: small_store_kernel<2, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 3: small_store_kernel<3, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 4: small_store_kernel<4, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 5: small_store_kernel<5, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 6: small_store_kernel<6, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        case 7: small_store_kernel<7, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
+        default: small_store_kernel<8, L32><<<grid, block, 0, stream>>>(KVPUB_ROW_ARGS); break;
     }
 #undef KVPUB_ROW_ARGS
+}
+
+static void launch_small(uint32_t num_replicas, uint32_t n, hipStream_t stream, const StoreParams& p) {
+    if (p.indexer_stride <= kMaxStride32) launch_small_l<true>(num_replicas, n, stream, p);
+    else launch_small_l<false>(num_replicas, n, stream, p);
 }
 
 hipError_t launch_store(const StoreParams& p, uint32_t num_replicas, hipStream_t stream) {
