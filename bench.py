@@ -40,21 +40,45 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "store_kernel_graph_T4096_R2_tra
 KERNEL_SOURCE = os.path.join(ROOT, "replicated_fp8_sparse_amd", "csrc", "store_kernel.hip")
 
 
-def measured_traffic():
-    """(HBM bytes per store launch, how) from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record, or (None, why) if the kernel source changed since."""
+def profile_record():
+    """The committed rocprofv3 record of the store kernel (FETCH_SIZE / WRITE_SIZE and
+    the kernel trace's durations), or (None, why) if the kernel source changed since."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_RECORD))
         src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except (OSError, ValueError):
-        return None, "no traffic record"
+        return None, "no profile record"
     if rec.get("source_sha256") != src:
-        return None, "the kernel source changed since the counters were taken"
+        return None, "the kernel source changed since the profile was taken"
+    return rec, None
+
+
+def measured_traffic():
+    """(HBM bytes per store launch, how) from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record, or (None, why) if the kernel source changed since."""
+    rec, why = profile_record()
+    if rec is None:
+        return None, why
     cal = rec["calibration"]
     return rec["traffic_bytes_per_launch"], (
         f"bytes per launch: rocprofv3 FETCH_SIZE x{cal['fetch_factor']} + WRITE_SIZE x{cal['write_factor']}, "
         "the factors from the floor kernel moving the same bytes (profiles/store_kernel_graph_T4096_R2_traffic.json)")
+
+
+def traced_durations():
+    """The store kernel's rocprofv3 kernel-trace durations from the committed record
+    (the roofline's launches: the store-only graph's timed replays), or None."""
+    rec, _ = profile_record()
+    if rec is None or "kernel_trace" not in rec:
+        return None
+    kt = rec["kernel_trace"]
+    return {"mean_us": round(kt["timed_replays_mean_ns"] / 1e3, 3), "p50_us": round(kt["timed_replays_p50_ns"] / 1e3, 3),
+            "dispatches": kt["dispatches"], "live_us_same_box": kt["live_us_same_box"],
+            "how": "rocprofv3 --kernel-trace of this benchmark (" + kt["summary"] + "); the tracer leaves 3-4 us "
+                   "between dispatches, so each one starts on an idle GPU (its XCDs start up to 1.4 us apart), "
+                   "which back-to-back replays do not; live_us_same_box is this line's avg_launch_us measured "
+                   "untraced on the box of the trace"}
 
 
 def alg_bytes(valid_tokens, replicas):
@@ -300,6 +324,7 @@ def main():
             "frac": round(store_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "traffic_unit": traffic_how,
+            "rocprof": traced_durations(),
             "alg_bytes_per_launch": store_bytes,
             "avg_launch_us": round(store_us, 3),
             "how": "HIP events around replays of a graph of the 61 store launches alone",
