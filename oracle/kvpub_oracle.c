@@ -412,6 +412,9 @@ static double e4m3_value(uint8_t c)
 static uint16_t float_to_bf16(float v)
 {
     uint16_t t = (uint16_t)(float_bits(v) >> 16);
+#if defined(KVO_PLANT) && KVO_PLANT == 20
+    if ((t & 0x7F80u) == 0) return (uint16_t)(t & 0x8000u);   /* planted: bf16 subnormals flushed */
+#endif
     double lo = (double)bf16_to_float(t), hi = (double)bf16_to_float((uint16_t)(t + 1u));
     double dl = (double)v - lo, dh = hi - (double)v;
     if (dl < 0) dl = -dl;
@@ -431,6 +434,10 @@ void kvo_dequant_tile(const uint8_t *codes, float scale, size_t n, uint16_t *out
     for (k = 0; k < n; ++k) {
         float v = (float)e4m3_value(codes[k]);       /* exact */
         float p = v * scale;                          /* one binary32 rounding */
+#if defined(KVO_PLANT) && KVO_PLANT == 19
+        if (p != 0.0f && p < 1.17549435e-38f && p > -1.17549435e-38f)
+            p = p < 0.0f ? -0.0f : 0.0f;              /* planted: subnormal products flushed */
+#endif
         out[k] = float_to_bf16(p);
     }
 }

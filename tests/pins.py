@@ -23,9 +23,11 @@ from the oracle itself:
   token order irrelevant, R replicas == R single-replica inserts.
 
 * the reader side (dequantizing gather): hand-derived products and their
-  bf16 rounding (``golden/gather_hand_values.txt``), a bit-exact round trip of
-  tiles whose values and scales are exact, the half-step error bound on random
-  rows, zero rows for padded and out-of-range slots.
+  bf16 rounding (``golden/gather_hand_values.txt``), every finite code times a
+  few hundred scales against integer round-to-nearest-even arithmetic, a
+  bit-exact round trip of tiles whose values and scales are exact, the
+  half-step error bound on random rows, zero rows for padded and out-of-range
+  slots.
 
 ``tests/test_oracle_plants.py`` builds copies of the oracle with planted
 mistakes and checks that at least one pin fails for each.
@@ -596,6 +598,84 @@ def pin_gather_roundtrip_exact(orc):
     assert np.array_equal(g_rope, rope), "RoPE bits not returned verbatim"
 
 
+def _rne_int(M, E, p, emin):
+    """M * 2^E (M a positive Python int, the value exact) rounded to p significant
+    bits, to nearest with ties to even, with the quantum at least 2^emin (the
+    subnormal range): returns (M2, E2), the rounded value being M2 * 2^E2."""
+    shift = max(M.bit_length() - p, emin - E)
+    if shift <= 0:
+        return M, E
+    q, r = M >> shift, M & ((1 << shift) - 1)
+    half = 1 << (shift - 1)
+    if r > half or (r == half and q & 1):
+        q += 1
+    return q, E + shift
+
+
+def _bf16_bits_of(neg, M, E):
+    """bf16 bit pattern of (-1)^neg * M * 2^E, M * 2^E already a bf16 value."""
+    sign = 0x8000 if neg else 0
+    if M == 0:
+        return sign
+    n = M.bit_length()
+    e = E + n - 1                                   # exponent of the leading bit
+    if e >= -126:
+        frac = (M << (8 - n)) & 0x7F if n <= 8 else (M >> (n - 8)) & 0x7F
+        return sign | ((e + 127) << 7) | frac
+    return sign | (M << (E + 133))                  # subnormal: M * 2^E = m * 2^-133
+
+
+def _dequant_want(code, scale):
+    """bf16 bits of RN_bf16(RN32(value(code) * scale)) with integer arithmetic only:
+    value(code) from the OCP E4M3 definition (exponent field E, mantissa M: E = 0 gives
+    M * 2^-9, else (8 + M) * 2^(E - 10)), scale from its binary32 fields."""
+    neg_c = bool(code & 0x80)
+    ef, mf = (code >> 3) & 15, code & 7
+    Mv, Ev = (mf, -9) if ef == 0 else (8 + mf, ef - 10)
+    u = int(np.float32(scale).view(np.uint32))
+    es, ms = (u >> 23) & 0xFF, u & 0x7FFFFF
+    Ms, Es = (ms, -149) if es == 0 else (ms | 0x800000, es - 150)
+    neg = neg_c != bool(u >> 31)
+    M, E = Mv * Ms, Ev + Es
+    if M == 0:
+        return 0x8000 if neg else 0
+    M, E = _rne_int(M, E, 24, -149)                 # the binary32 product
+    if M == 0:
+        return 0x8000 if neg else 0
+    M, E = _rne_int(M, E, 8, -133)                  # then bf16
+    return _bf16_bits_of(neg, M, E)
+
+
+def pin_gather_dequant_exhaustive(orc):
+    """Every finite e4m3 code (254 patterns, both signs, subnormal codes included)
+    times each of about 330 scales -- powers of two from 2^-140 to 2^110, random
+    binary32 values over the same range, binary32 subnormals, and RN32(amax / 448)
+    of random bf16 amax (the scales a store writes) -- dequantizes to
+    RN_bf16(RN32(value * scale)) bit for bit, against integer round-to-nearest-even
+    arithmetic written from the definitions (products whose binary32 or bf16
+    result is subnormal included)."""
+    from fractions import Fraction
+    from exact_fp import rn32
+    rng = np.random.default_rng(23)
+    scales = [2.0 ** k for k in range(-140, 111, 5)]
+    ex = rng.integers(-130, 100, 200)
+    scales += [float(np.float32(rng.uniform(1.0, 2.0) * 2.0 ** int(k))) for k in ex]
+    scales += [float(np.array([int(v)], np.uint32).view(np.float32)[0]) for v in rng.integers(1, 1 << 23, 20)]
+    amax = rng.integers(1, 0x7F80, 60).astype(np.uint16)
+    scales += [rn32(Fraction(float(bf16_to_f32(a))) / 448) for a in amax]
+    scales = [s for s in scales if s > 0]
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    subnormal_out = 0
+    for s in scales:
+        got = orc.dequant_tile(codes, np.float32(s))
+        want = np.array([_dequant_want(int(c), s) for c in codes], np.uint16)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"{bad.size} codes at scale {float(np.float32(s)).hex()} differ, e.g. " + ", ".join(
+            f"{codes[i]:#04x}: {got[i]:#06x} want {want[i]:#06x}" for i in bad[:4])
+        subnormal_out += int(np.count_nonzero(((want & 0x7F80) == 0) & ((want & 0x7F) != 0)))
+    assert subnormal_out > 0, "no product with a bf16-subnormal result swept"
+
+
 def pin_gather_bound_and_pads(orc):
     """Random rows: the gathered value is within half an e4m3 step (at the tile
     scale) of the input, plus the binary32 and bf16 roundings; padded and
@@ -632,4 +712,5 @@ ALL_PINS = [pin_hand_codes, pin_encoder_bruteforce, pin_encoder_torch, pin_encod
             pin_tile_exact, pin_tile_invariants, pin_tile_nearest, pin_tile_special,
             pin_tile_scale_exact, pin_tile_quotient_sweep,
             pin_layout, pin_layout_order_and_fanout, pin_store_empty, pin_epoch,
-            pin_gather_hand_values, pin_gather_roundtrip_exact, pin_gather_bound_and_pads]
+            pin_gather_hand_values, pin_gather_roundtrip_exact, pin_gather_dequant_exhaustive,
+            pin_gather_bound_and_pads]

@@ -7,13 +7,13 @@ scale offset, page and offset swapped, pads counted as invalid, a replica
 skipped, a wrong subnormal step, truncation instead of rounding, the tile
 scale as a multiply by RN(1/448), the quotient as a multiply by RN(1/scale); on the
 reader side a sign dropped on decode, bf16 truncation, scales of the wrong
-tile."""
+tile, subnormal binary32 products flushed to zero, bf16 subnormals flushed."""
 import pytest
 
 import oracle
 import pins
 
-PLANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18]
+PLANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 20]
 
 
 @pytest.mark.parametrize("plant", PLANTS)
