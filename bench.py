@@ -677,7 +677,70 @@ def gather_line(torch, kvpub, ctx, slots, T, valid, stream):
             "cold_launch_us": round(cold, 3),
             "how": "replays of a graph of 61 gathers over the 61 layer caches of replica 0 (avg), the same "
                    "launches eagerly back to back (eager, host launch cost included), and single launches "
-                   "after a 1 GiB read (cold); bytes = 788 B read + 1408 B written per token"}
+                   "after a 1 GiB read (cold); bytes = 788 B read + 1408 B written per token",
+            "decode": gather_decode(torch, kvpub, ctx, stream),
+            "topk": gather_topk(torch, kvpub, ctx, stream)}
+
+
+def graph_launch_us(torch, stream, launch, n, reps):
+    """Average microseconds per launch of a replayed torch graph of launch(0..n-1)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                launch(i)
+        for _ in range(2):
+            g.replay()
+        with Timer(torch, stream) as t:
+            for _ in range(reps):
+                g.replay()
+    del g
+    return t.ms * 1e3 / (reps * n)
+
+
+def gather_outputs(torch, T):
+    return (torch.empty((T, 512), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((T, 64), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((T, 128), dtype=torch.bfloat16, device="cuda"))
+
+
+def gather_decode(torch, kvpub, ctx, stream):
+    """The gather at a decode step's size: the decode workload's 64 slots (3 padded)
+    from each of the 61 layer caches, beside an empty kernel of the same grid."""
+    from replicated_fp8_sparse_amd import workloads as W
+    sh = stream.cuda_stream
+    sl = W.decode(layers=1)[1][0].slots
+    T, L = sl.size, 61
+    slots = torch.from_numpy(sl).to("cuda")
+    lat, rope, idx = gather_outputs(torch, T)
+    us = graph_launch_us(torch, stream, lambda l: kvpub.check(kvpub.kvpub_gather(
+        ctx, 0, l, T, slots.data_ptr(), lat.data_ptr(), 512, rope.data_ptr(), 64, idx.data_ptr(), 128, sh)), L, 8)
+    empty = empty_node_us(torch, stream, L, (T + 15) // 16, 256)
+    return {"tokens": T, "avg_launch_us": round(us, 3), "empty_node_us": round(empty, 3),
+            "how": "replays of a graph of 61 gathers of the decode workload's 64 slots (one per layer cache); "
+                   "empty_node_us: the same graph of an empty kernel with the gather's grid (4 blocks of 256 threads)"}
+
+
+def gather_topk(torch, kvpub, ctx, stream, layers=8):
+    """The decode-time read pattern: 16 requests each selecting 2048 distinct slots of
+    their own 512-page context (32,768 scattered rows), one launch per layer cache."""
+    from replicated_fp8_sparse_amd import workloads as W
+    sh = stream.cuda_stream
+    sl = W.topk_slots()
+    T = sl.size
+    slots = torch.from_numpy(sl).to("cuda")
+    lat, rope, idx = gather_outputs(torch, T)
+    us = graph_launch_us(torch, stream, lambda l: kvpub.check(kvpub.kvpub_gather(
+        ctx, 0, l, T, slots.data_ptr(), lat.data_ptr(), 512, rope.data_ptr(), 64, idx.data_ptr(), 128, sh)),
+        layers, 4)
+    b = T * (GATHER_READ_BYTES_PER_TOKEN + GATHER_WRITE_BYTES_PER_TOKEN)
+    del lat, rope, idx
+    torch.cuda.empty_cache()
+    return {"tokens": T, "requests": 16, "k": 2048, "context_pages": 512, "avg_launch_us": round(us, 2),
+            "alg_bytes": b, "gbps": round(b / (us * 1e-6) / 1e9, 1),
+            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "how": f"replays of a graph of {layers} gathers, one per layer cache of replica 0, each reading the "
+                   "32,768 rows of the top-k slot lists (each layer's 8192 pages covered by the 16 contexts)"}
 
 
 def cold_launch_us(torch, stream, launch, copies, n=12):

@@ -262,3 +262,30 @@ def test_gather_graph_layer_full_size(orc):
             check(out, oracle_gather(orc, dev, replica, 0, slots), f"graph layer, replica {replica}")
     finally:
         dev.free()
+
+
+def test_gather_topk_pattern(orc):
+    """The decode-time read pattern at the size the benchmark times it: 16 requests,
+    each selecting 2,048 distinct slots of its own 512-page context, gathered as one
+    launch of 32,768 slots from one layer of the graph workload's cache (R=2, 8,192
+    pages).  Half of the selected slots hold rows stored by kvpub_store, the rest the
+    fill bytes (valid codes and scales all the same); bit for bit against the
+    oracle's gather of the same replica bytes."""
+    rng = np.random.default_rng(909)
+    layout = W.CacheLayout(replicas=2, layers=1, num_pages=W.graph_layout().num_pages)
+    slots = W.topk_slots()
+    T = slots.size
+    stored = rng.permutation(slots)[:T // 2]
+    x = W.LayerInputs(*W._normal_rows(rng, stored.size), stored)
+    log(f"gather, top-k pattern: T={T} (16 x 2048), stored {stored.size}, R=2, pages={layout.num_pages}")
+    dev = DeviceCache(layout)
+    try:
+        kvpub.check(dev.store(0, DeviceInputs(x)), "kvpub_store")
+        out = Outputs(T)
+        kvpub.check(gather(dev, out, 1, 0, to_dev_i64(slots), T), "kvpub_gather")
+        check(out, oracle_gather(orc, dev, 1, 0, slots), "top-k pattern, replica 1")
+        st, invalid, _ = dev.errors(clear=True)
+        kvpub.check(st)
+        assert invalid == 0
+    finally:
+        dev.free()

@@ -163,3 +163,21 @@ def test_rotation_slots_write_disjoint_pages():
         runs = np.split(s[:8155], np.nonzero(np.diff(s[:8155]) != 1)[0] + 1)
         assert all(r[0] % 64 == 0 for r in runs)                    # runs start at page boundaries
         assert sum(r.size for r in runs) == 8155
+
+
+def test_topk_slots_recipe():
+    """Each request's k slots are distinct, lie in its own context's pages, and the
+    contexts of the default recipe cover the graph layer's pages once."""
+    s = W.topk_slots()
+    assert s.dtype == np.int64 and s.shape == (16 * 2048,)
+    assert digest(s) == digest(W.topk_slots()) and digest(s) != digest(W.topk_slots(seed=7))
+    cap = W.graph_layout().capacity
+    assert s.min() >= 0 and s.max() < cap
+    for q, r in enumerate(s.reshape(16, 2048)):
+        assert np.unique(r).size == r.size
+        pages = r // 64
+        assert pages.min() >= q * 512 and pages.max() < (q + 1) * 512
+        assert not np.all(np.diff(r) > 0), "a request's slots come in random order"
+    small = W.topk_slots(requests=3, k=100, context_pages=4, num_pages=10)
+    assert set((small // 64).tolist()) <= set(range(10))
+    assert set((small[200:] // 64).tolist()) <= {8, 9, 0, 1}   # request 2 wraps around
