@@ -196,8 +196,8 @@ KVPUB_API kvpub_status kvpub_create_static(const kvpub_config *cfg, void *const 
  *   indexer: bf16 [T, 128], row stride indexer_row_stride elements
  *   slot_mapping: int64 [T] device array (-1 = padded token)
  * Inputs are device pointers, 16-byte aligned, with row strides that are
- * multiples of 8 elements and at least the row width; slot_mapping is 8-byte
- * aligned.  Valid slots within one call must be distinct and inputs finite.
+ * multiples of 8 elements, at least the row width and at most 2^31 - 1
+ * elements; slot_mapping is 8-byte aligned.  Valid slots within one call must be distinct and inputs finite.
  * num_tokens == 0 returns KVPUB_OK and launches nothing.  No allocation and no
  * synchronization: safe under stream capture.  Inputs must stay alive until
  * the stream work completes. */
@@ -222,8 +222,8 @@ KVPUB_API kvpub_status kvpub_store(kvpub_ctx *ctx, uint32_t layer, int64_t num_t
  *   indexer_out: bf16 [T, 128], row stride indexer_row_stride elements
  *   slot_mapping: int64 [T] device array
  * Outputs are caller-owned device buffers, 16-byte aligned, row strides
- * multiples of 8 elements and at least the row width; slot_mapping is 8-byte
- * aligned.  Only the output rows are written; the cache is only read.  A
+ * multiples of 8 elements, at least the row width and at most 2^31 - 1
+ * elements; slot_mapping is 8-byte aligned.  Only the output rows are written; the cache is only read.  A
  * context poisoned by a fence timeout still gathers (reading publishes
  * nothing).  num_tokens == 0 returns KVPUB_OK and launches nothing.  No
  * allocation and no synchronization: safe under stream capture.  Argument

@@ -165,6 +165,7 @@ def test_gather_bad_arguments():
     assert g(r=2) == bad and g(l=2) == bad and g(T=-1) == bad
     assert g(sl=0) == bad and g(lat=0) == bad and g(lat=out.lat.data_ptr() + 2) == bad
     assert g(ls=511) == bad and g(ls=500) == bad and g(rs=60) == bad
+    assert g(ls=1 << 31) == bad and g(rs=1 << 31) == bad                    # strides above 2^31 - 1
     assert g(T=0) == kvpub.KVPUB_OK
     torch().cuda.synchronize()
     assert np.all(out.host()[0] == CANARY), "a rejected call wrote output"

@@ -304,6 +304,9 @@ def test_bad_arguments_write_nothing(orc):
             (dev.ctx, 0, 16, p[0] + 2, 512, p[1], 64, p[2], 128, p[3], s),            # misaligned
             (dev.ctx, 0, 16, p[0], 511, p[1], 64, p[2], 128, p[3], s),                # stride < row
             (dev.ctx, 0, 16, p[0], 516, p[1], 64, p[2], 128, p[3], s),                # stride % 8
+            (dev.ctx, 0, 16, p[0], 1 << 31, p[1], 64, p[2], 128, p[3], s),            # stride >= 2^31
+            (dev.ctx, 0, 16, p[0], 512, p[1], 1 << 31, p[2], 128, p[3], s),
+            (dev.ctx, 0, 16, p[0], 512, p[1], 64, p[2], 1 << 31, p[3], s),
             (dev.ctx, 0, 16, p[0], 512, p[1], 64, p[2], 128, 0, s),                   # null slots
             (None, 0, 16, p[0], 512, p[1], 64, p[2], 128, p[3], s),                   # null ctx
         ]
