@@ -61,6 +61,10 @@
  * Argument problems are reported before anything is launched, so nothing is
  * written.  Device-side problems (invalid slots, a fence that timed out) are
  * recorded in the context's device words and reported by kvpub_error_read.
+ *
+ * Logging: with the environment variable KVPUB_LOG=1 (read once), every
+ * kvpub_create, kvpub_create_static and kvpub_destroy of a context prints one
+ * line to stderr with its configuration and status; no other call logs.
  */
 #ifndef KVPUB_H
 #define KVPUB_H

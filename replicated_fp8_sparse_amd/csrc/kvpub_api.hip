@@ -5,6 +5,7 @@
 // succeeds at startup or leaves nothing behind; teardown drops every view).
 #include <algorithm>
 #include <cstddef>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -190,6 +191,26 @@ void release(kvpub_ctx* c) {
     delete c;
 }
 
+// KVPUB_LOG=1: one line on stderr for each context created or destroyed (never
+// on the store / fence / gather path).
+bool log_enabled() {
+    static const bool on = [] {
+        const char* s = std::getenv("KVPUB_LOG");
+        return s != nullptr && s[0] == '1';
+    }();
+    return on;
+}
+
+void log_create(const char* what, const kvpub_config* cfg, kvpub_status st, const kvpub_ctx* c) {
+    if (!log_enabled()) return;
+    if (cfg && cfg->struct_size == sizeof(kvpub_config))
+        std::fprintf(stderr, "kvpub: %s R=%u L=%u pages=%llu lanes=%u participants=%u device=%d flags=%u -> %s (ctx %p)\n",
+                     what, cfg->num_replicas, cfg->num_layers, (unsigned long long)cfg->num_pages, cfg->num_lanes,
+                     cfg->num_participants, cfg->device, cfg->flags, kvpub_strerror(st), (const void*)c);
+    else
+        std::fprintf(stderr, "kvpub: %s (no valid config) -> %s\n", what, kvpub_strerror(st));
+}
+
 kvpub_status sync_device() {
     return map_hip(hipDeviceSynchronize());
 }
@@ -315,8 +336,8 @@ KVPUB_API void kvpub_config_init(kvpub_config* cfg, uint32_t num_replicas, uint3
     cfg->flags = 0;
 }
 
-KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_bases,
-                                   void* const* idx_bases, kvpub_ctx** out) {
+static kvpub_status create_ctx(const kvpub_config* cfg, void* const* main_bases, void* const* idx_bases,
+                               kvpub_ctx** out) {
     if (!out) return KVPUB_ERR_INVALID_ARG;
     *out = nullptr;
     kvpub_status st = check_config(cfg);
@@ -378,8 +399,15 @@ KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_b
     return KVPUB_OK;
 }
 
-KVPUB_API kvpub_status kvpub_create_static(const kvpub_config* cfg, void* const* main_bases,
-                                          void* const* idx_bases, kvpub_stream_t stream, kvpub_ctx** out) {
+KVPUB_API kvpub_status kvpub_create(const kvpub_config* cfg, void* const* main_bases,
+                                   void* const* idx_bases, kvpub_ctx** out) {
+    const kvpub_status st = create_ctx(cfg, main_bases, idx_bases, out);
+    log_create("create", cfg, st, out ? *out : nullptr);
+    return st;
+}
+
+static kvpub_status create_static_ctx(const kvpub_config* cfg, void* const* main_bases, void* const* idx_bases,
+                                      kvpub_stream_t stream, kvpub_ctx** out) {
     if (!out) return KVPUB_ERR_INVALID_ARG;
     *out = nullptr;
     kvpub_status st = check_config(cfg);
@@ -434,6 +462,13 @@ KVPUB_API kvpub_status kvpub_create_static(const kvpub_config* cfg, void* const*
     slot.in_use = true;
     *out = c;
     return KVPUB_OK;
+}
+
+KVPUB_API kvpub_status kvpub_create_static(const kvpub_config* cfg, void* const* main_bases,
+                                          void* const* idx_bases, kvpub_stream_t stream, kvpub_ctx** out) {
+    const kvpub_status st = create_static_ctx(cfg, main_bases, idx_bases, stream, out);
+    log_create("create_static", cfg, st, out ? *out : nullptr);
+    return st;
 }
 
 KVPUB_API kvpub_status kvpub_store(kvpub_ctx* ctx, uint32_t layer, int64_t num_tokens,
@@ -632,12 +667,14 @@ KVPUB_API kvpub_status kvpub_participant_signal(kvpub_ctx* ctx, uint32_t lane, u
 
 KVPUB_API kvpub_status kvpub_destroy(kvpub_ctx* ctx) {
     if (!ctx) return KVPUB_OK;
+    const void* id = ctx;
     kvpub_status st;
     {
         DeviceGuard guard(ctx->cfg.device);
         st = sync_device();
         release(ctx);
     }
+    if (log_enabled()) std::fprintf(stderr, "kvpub: destroy ctx %p -> %s\n", id, kvpub_strerror(st));
     return st;
 }
 

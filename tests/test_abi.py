@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -192,3 +193,24 @@ def test_floor_library_exports_its_header():
     assert e(1, 32) == 1 and e(1, 100) == 1                # not a multiple of 64 threads
     assert e(1, 2048) == 1                                 # more than 1024 threads
     assert e(1 << 31, 64) == 1                             # grid too large
+
+
+def test_log_lines_only_when_asked():
+    """KVPUB_LOG=1 prints one line per context creation (its configuration and
+    status) on stderr; without it the library prints nothing."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from replicated_fp8_sparse_amd import kvpub\n"
+            "cfg = kvpub.kvpub_config_init(2, 1, 4); cfg.num_replicas = 0\n"
+            "st, ctx = kvpub.kvpub_create(cfg, [16, 32], [16, 32])\n"
+            "assert st == kvpub.KVPUB_ERR_INVALID_ARG and ctx is None\n"
+            "assert kvpub.kvpub_destroy(None) == kvpub.KVPUB_OK\n") % ROOT
+    env = {k: v for k, v in os.environ.items() if k != "KVPUB_LOG"}
+    quiet = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert quiet.returncode == 0, quiet.stderr
+    assert "kvpub:" not in quiet.stderr
+    loud = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                          env=dict(env, KVPUB_LOG="1"), timeout=120)
+    assert loud.returncode == 0, loud.stderr
+    lines = [l for l in loud.stderr.splitlines() if l.startswith("kvpub:")]
+    assert lines == ["kvpub: create R=0 L=1 pages=4 lanes=1 participants=1 device=0 flags=0 -> invalid argument "
+                     "(ctx (nil))"], loud.stderr
