@@ -214,3 +214,19 @@ def test_log_lines_only_when_asked():
     lines = [l for l in loud.stderr.splitlines() if l.startswith("kvpub:")]
     assert lines == ["kvpub: create R=0 L=1 pages=4 lanes=1 participants=1 device=0 flags=0 -> invalid argument "
                      "(ctx (nil))"], loud.stderr
+
+
+def test_valid_calls_without_a_device_fail_cleanly():
+    """A valid configuration on a machine with no usable GPU: creation returns a HIP
+    (or unsupported-device) status and no handle, and nothing is left to release."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: creation would succeed")
+    no_device = (kvpub.KVPUB_ERR_HIP, kvpub.KVPUB_ERR_UNSUPPORTED)
+    cfg = kvpub.kvpub_config_init(2, 3, 8)
+    st, ctx = kvpub.kvpub_create(cfg, [1 << 20, 2 << 20], [3 << 20, 4 << 20])
+    assert st in no_device and ctx is None
+    st, ctx = kvpub.kvpub_create_static(cfg, [1 << 20, 2 << 20], [3 << 20, 4 << 20])
+    assert st in no_device and ctx is None
+    st, vmm, _, _ = kvpub.kvpub_vmm_create(kvpub.kvpub_config_init(2, 3, 8), 16)
+    assert st in no_device and vmm is None
