@@ -55,16 +55,20 @@ def orc_epoch(orc, e0, n):
 def test_lanes_advance_independently():
     import torch
     layout = CacheLayout(replicas=1, layers=1, num_pages=1)
-    dev = G.DeviceCache(layout, lanes=3)
+    dev = G.DeviceCache(layout, lanes=64)
     try:
-        G.log("lanes: 10 fences on lane 0 (stream A), 7 on lane 2 (stream B)")
+        G.log("lanes: 64 lanes; 10 fences on lane 0 (stream A), 7 on lane 2 (stream B), 3 on lane 63")
         a, b = torch.cuda.Stream(), torch.cuda.Stream()
         for _ in range(10):
             kvpub.check(dev.fence(0, a))
         for _ in range(7):
             kvpub.check(dev.fence(2, b))
+        for _ in range(3):
+            kvpub.check(dev.fence(63, b))
         torch.cuda.synchronize()
-        assert (dev.epoch(0), dev.epoch(1), dev.epoch(2)) == (10, 0, 7)
+        want = {0: 10, 2: 7, 63: 3}
+        assert [dev.epoch(l) for l in range(64)] == [want.get(l, 0) for l in range(64)]
+        assert dev.fence(64, a) == kvpub.KVPUB_ERR_INVALID_ARG
     finally:
         dev.free()
 
