@@ -283,15 +283,17 @@ def main():
     log("verifying the timed steps' output")
     check = verify_graph_output(torch, layout, main_bufs, idx_bufs, slots_np, layer=L // 2)
 
-    gather = None if args.no_extras else gather_line(torch, kvpub, ctx, slots, T, valid, stream)
-    floor_graph = None if args.no_extras else floor_graph_layer(torch, stream, L, T, valid, R, store_us)
+    gather = None if args.no_extras else aux_leg("gather", lambda: gather_line(torch, kvpub, ctx, slots, T, valid,
+                                                                               stream))
+    floor_graph = None if args.no_extras else aux_leg("floor", lambda: floor_graph_layer(torch, stream, L, T, valid,
+                                                                                        R, store_us))
 
     extras = {}
     decode = fanout = None
     if not args.no_extras:
         extras = store_only_extras(torch, kvpub, W, stream, vmm=not args.no_vmm)
-        decode = decode_eager(torch, kvpub, W, stream)
-        fanout = fanout_ab(torch, kvpub, W, stream)
+        decode = aux_leg("decode", lambda: decode_eager(torch, kvpub, W, stream))
+        fanout = aux_leg("fan-out A/B", lambda: fanout_ab(torch, kvpub, W, stream))
 
     traffic, traffic_how = measured_traffic()
     result = {
@@ -361,6 +363,17 @@ def main():
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def aux_leg(name, fn):
+    """Run one auxiliary measurement (not the timed steps, their verification or the
+    oracle comparison, which stay fatal).  An exception there is recorded in the
+    line as {"error": ...} instead of losing the line."""
+    try:
+        return fn()
+    except Exception as e:  # noqa: BLE001 -- reported, not hidden
+        log(f"{name} failed: {type(e).__name__}: {e}")
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def written_offsets(torch, layout, layer, slots_np):
@@ -488,84 +501,91 @@ def store_only_extras(torch, kvpub, W, stream, vmm=True):
     dirty line behind.  The heavy shape runs again on VMM-backed replicas."""
     from replicated_fp8_sparse_amd import floor as _fl  # noqa: F401  (fails loudly if unbuilt)
     out = {}
-    sh = stream.cuda_stream
     shapes = [("prefill_T8192_R4", W.prefill, False), ("heavy_T32768_R4", W.heavy, False)]
     if vmm:
         shapes.append(("heavy_T32768_R4_vmm", W.heavy, True))
     for name, fn, vmm in shapes:
-        layout, x = fn()
-        rot = W.prefill_rotation_slots(16) if fn is W.prefill else W.heavy_rotation_slots(8)
-        copies = len(rot)
-        log(f"store-only {name}")
-        R = layout.replicas
-        cfg = kvpub.kvpub_config_init(R, 1, layout.num_pages)
-        storage = None
-        if vmm:
-            # the store never reads the cache, so the VMM pages need no fill for timing
-            st, storage, mbp, ibp = kvpub.kvpub_vmm_create(cfg, layout.num_pages)
-            kvpub.check(st, "kvpub_vmm_create")
-            mb = ib = None
-        else:
-            mb = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
-            ib = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
-            for b in mb:
-                layout.fill_device(b, "main")
-            for b in ib:
-                layout.fill_device(b, "idx")
-            mbp, ibp = [b.data_ptr() for b in mb], [b.data_ptr() for b in ib]
-        st, ctx = kvpub.kvpub_create(cfg, mbp, ibp)
-        kvpub.check(st)
-        T = x.slots.size
-        lat = torch.from_numpy(x.latent.view(np.int16)).to("cuda").repeat(copies, 1, 1)
-        rope = torch.from_numpy(x.rope.view(np.int16)).to("cuda").repeat(copies, 1, 1)
-        idx = torch.from_numpy(x.indexer.view(np.int16)).to("cuda").repeat(copies, 1, 1)
-        slots = torch.from_numpy(np.stack(rot)).to("cuda")
-        same = torch.from_numpy(x.slots).to("cuda")
-        valid = int(((x.slots >= 0) & (x.slots < layout.capacity)).sum())
-        assert all(int(((s >= 0) & (s < layout.capacity)).sum()) == valid for s in rot)
-
-        def launch(c, slot_ptr=None):
-            return kvpub.kvpub_store(ctx, 0, T, lat[c].data_ptr(), 512, rope[c].data_ptr(), 64,
-                                     idx[c].data_ptr(), 128, slots[c].data_ptr() if slot_ptr is None else slot_ptr, sh)
-
-        def warm(body):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(stream):
-                with torch.cuda.graph(g, stream=stream):
-                    for c in range(copies):
-                        kvpub.check(body(c))
-                g.replay()
-                reps = 8
-                with Timer(torch, stream) as tm:
-                    for _ in range(reps):
-                        g.replay()
-            del g
-            return tm.ms * 1e3 / (reps * copies)
-
-        us = warm(launch)
-        us_same = warm(lambda c: launch(c, same.data_ptr()))
-        cold = cold_launch_us(torch, stream, launch, copies)
-        b = alg_bytes(valid, R)
-        gb = lambda t: b / (t * 1e-6) / 1e9
-        out[name] = {"avg_launch_us": round(us, 3), "alg_bytes": b,
-                     "gbps": round(gb(us), 1), "frac": round(gb(us) / HBM_PEAK_GBPS, 4),
-                     "tokens_per_s": round(valid / (us * 1e-6), 1),
-                     "cold_launch_us": round(cold, 3), "cold_frac": round(gb(cold) / HBM_PEAK_GBPS, 4),
-                     "same_slots_launch_us": round(us_same, 3),
-                     "storage": "vmm" if vmm else "device allocations",
-                     "how": f"warm: a replayed graph of {copies} launches over rotated input copies and slot "
-                            "mappings writing disjoint page sets (bytes touched per replay exceed the 256 MB "
-                            "memory-side cache); cold: median of single launches, each after reading a 1 GiB "
-                            "buffer (no dirty lines left); same_slots: the warm graph with one slot mapping "
-                            "(rewrites the same pages every launch)"}
-        if not vmm:
-            out[name]["floor"] = floor_line(torch, stream, valid, R, copies, us)
-        kvpub.check(kvpub.kvpub_destroy(ctx))
-        if storage is not None:
-            kvpub.check(kvpub.kvpub_vmm_destroy(storage), "kvpub_vmm_destroy")
-        del mb, ib, lat, rope, idx
-        torch.cuda.empty_cache()
+        out[name] = aux_leg(f"store-only {name}", lambda: store_only_shape(torch, kvpub, W, stream, name, fn, vmm))
     return out
+
+
+def store_only_shape(torch, kvpub, W, stream, name, fn, vmm):
+    """One shape of store_only_extras: warm, same-slots and cold launch times, and
+    (device allocations) the plain-stream floor for the same bytes."""
+    sh = stream.cuda_stream
+    layout, x = fn()
+    rot = W.prefill_rotation_slots(16) if fn is W.prefill else W.heavy_rotation_slots(8)
+    copies = len(rot)
+    log(f"store-only {name}")
+    R = layout.replicas
+    cfg = kvpub.kvpub_config_init(R, 1, layout.num_pages)
+    storage = None
+    if vmm:
+        # the store never reads the cache, so the VMM pages need no fill for timing
+        st, storage, mbp, ibp = kvpub.kvpub_vmm_create(cfg, layout.num_pages)
+        kvpub.check(st, "kvpub_vmm_create")
+        mb = ib = None
+    else:
+        mb = [torch.empty(layout.main_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        ib = [torch.empty(layout.idx_bytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        for b in mb:
+            layout.fill_device(b, "main")
+        for b in ib:
+            layout.fill_device(b, "idx")
+        mbp, ibp = [b.data_ptr() for b in mb], [b.data_ptr() for b in ib]
+    st, ctx = kvpub.kvpub_create(cfg, mbp, ibp)
+    kvpub.check(st)
+    T = x.slots.size
+    lat = torch.from_numpy(x.latent.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+    rope = torch.from_numpy(x.rope.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+    idx = torch.from_numpy(x.indexer.view(np.int16)).to("cuda").repeat(copies, 1, 1)
+    slots = torch.from_numpy(np.stack(rot)).to("cuda")
+    same = torch.from_numpy(x.slots).to("cuda")
+    valid = int(((x.slots >= 0) & (x.slots < layout.capacity)).sum())
+    assert all(int(((s >= 0) & (s < layout.capacity)).sum()) == valid for s in rot)
+
+    def launch(c, slot_ptr=None):
+        return kvpub.kvpub_store(ctx, 0, T, lat[c].data_ptr(), 512, rope[c].data_ptr(), 64,
+                                 idx[c].data_ptr(), 128, slots[c].data_ptr() if slot_ptr is None else slot_ptr, sh)
+
+    def warm(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for c in range(copies):
+                    kvpub.check(body(c))
+            g.replay()
+            reps = 8
+            with Timer(torch, stream) as tm:
+                for _ in range(reps):
+                    g.replay()
+        del g
+        return tm.ms * 1e3 / (reps * copies)
+
+    us = warm(launch)
+    us_same = warm(lambda c: launch(c, same.data_ptr()))
+    cold = cold_launch_us(torch, stream, launch, copies)
+    b = alg_bytes(valid, R)
+    gb = lambda t: b / (t * 1e-6) / 1e9
+    res = {"avg_launch_us": round(us, 3), "alg_bytes": b,
+                 "gbps": round(gb(us), 1), "frac": round(gb(us) / HBM_PEAK_GBPS, 4),
+                 "tokens_per_s": round(valid / (us * 1e-6), 1),
+                 "cold_launch_us": round(cold, 3), "cold_frac": round(gb(cold) / HBM_PEAK_GBPS, 4),
+                 "same_slots_launch_us": round(us_same, 3),
+                 "storage": "vmm" if vmm else "device allocations",
+                 "how": f"warm: a replayed graph of {copies} launches over rotated input copies and slot "
+                        "mappings writing disjoint page sets (bytes touched per replay exceed the 256 MB "
+                        "memory-side cache); cold: median of single launches, each after reading a 1 GiB "
+                        "buffer (no dirty lines left); same_slots: the warm graph with one slot mapping "
+                        "(rewrites the same pages every launch)"}
+    if not vmm:
+        res["floor"] = floor_line(torch, stream, valid, R, copies, us)
+    kvpub.check(kvpub.kvpub_destroy(ctx))
+    if storage is not None:
+        kvpub.check(kvpub.kvpub_vmm_destroy(storage), "kvpub_vmm_destroy")
+    del mb, ib, lat, rope, idx
+    torch.cuda.empty_cache()
+    return res
 
 
 def fanout_ab(torch, kvpub, W, stream):

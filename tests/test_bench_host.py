@@ -67,3 +67,13 @@ def test_more_than_one_gpu_exits_with_a_message(argv, env):
                        env=e, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_an_auxiliary_leg_that_fails_is_recorded_not_fatal(capsys):
+    assert bench.aux_leg("ok leg", lambda: {"x": 1}) == {"x": 1}
+
+    def broken():
+        raise RuntimeError("no VMM on this device")
+
+    assert bench.aux_leg("vmm leg", broken) == {"error": "RuntimeError: no VMM on this device"}
+    assert "vmm leg failed" in capsys.readouterr().err
